@@ -1,0 +1,295 @@
+"""Byte and FLOP ledger of the prologue (host-side bookkeeping, no device work).
+
+Two models from the tilelang-tutorial pages are restated here so that the
+measurements can be put next to them, plus the algorithmic byte count that
+this library's GB/s figures use as their numerator.
+
+* Chapter 13 ledger page (``ledger.py``): one kernel reads each input once
+  and writes each output once; an intermediate tensor counts as a write of
+  one kernel and a read of the next; add/sub/mul/div/max and each
+  transcendental count one FLOP. Five unfused/fused plan pairs are modelled.
+* Chapter 28 case-study page (``case_norm_rope_quant.py``): the QK-norm +
+  RoPE + fp8 operator, its FLOP rule, its payload bytes, and the lookup
+  bytes (norm weights and the cos/sin table) under three block designs:
+  A = one row per block, B = a few rows per block, C = one token per block.
+
+The chapter-28 model counts the table as 2 * tokens * head_dim * 4 bytes
+(cos and sin at full head width); this library's boundary takes half-width
+tables ``[tokens, rope_dim/2]`` so its own count (``qk_bytes``) is smaller.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+__all__ = [
+    "ELEM_BYTES",
+    "Tensor",
+    "Kernel",
+    "Plan",
+    "p4_plans",
+    "QKShape",
+    "p3_design",
+    "p3_designs",
+    "p3_ideal_bytes",
+    "p3_flops",
+    "qk_bytes",
+    "norm_rope_bytes",
+    "rmsnorm_fwd_bytes",
+    "rmsnorm_bwd_bytes",
+    "qk_flops",
+]
+
+ELEM_BYTES = {"float32": 4, "float16": 2, "bfloat16": 2, "float8_e4m3fn": 1}
+
+
+# ----------------------------------------------------------- chapter 13 ledger model
+
+
+@dataclasses.dataclass(frozen=True)
+class Tensor:
+    name: str
+    numel: int
+    dtype: str
+
+    def __post_init__(self):
+        if self.dtype not in ELEM_BYTES:
+            raise ValueError(f"unknown dtype {self.dtype!r}")
+        if self.numel < 0:
+            raise ValueError(f"{self.name}: negative element count")
+
+    @property
+    def nbytes(self) -> int:
+        return self.numel * ELEM_BYTES[self.dtype]
+
+
+@dataclasses.dataclass(frozen=True)
+class Kernel:
+    name: str
+    reads: tuple
+    writes: tuple
+    flops: int
+
+    @property
+    def moved(self) -> int:
+        return sum(t.nbytes for t in self.reads) + sum(t.nbytes for t in self.writes)
+
+
+@dataclasses.dataclass(frozen=True)
+class Plan:
+    name: str
+    kernels: tuple
+
+    @property
+    def moved(self) -> int:
+        return sum(k.moved for k in self.kernels)
+
+    @property
+    def flops(self) -> int:
+        return sum(k.flops for k in self.kernels)
+
+    @property
+    def ai(self) -> float:
+        return self.flops / self.moved if self.moved else math.inf
+
+
+def _scale_add(n: int, dt: str):
+    x, b, t, y = (Tensor(s, n, dt) for s in "xbty")
+    return (
+        Plan("scale+add, 2 kernels", (Kernel("t=x*a", (x,), (t,), n), Kernel("y=t+b", (t, b), (y,), n))),
+        Plan("scale+add, fused", (Kernel("y=x*a+b", (x, b), (y,), 2 * n),)),
+    )
+
+
+def _rmsnorm(m: int, n: int, dt: str):
+    x, w, y = Tensor("x", m * n, dt), Tensor("w", n, dt), Tensor("y", m * n, dt)
+    sq, sc = Tensor("x2", m * n, dt), Tensor("scaled", m * n, dt)
+    mean, mean_eps, rstd = (Tensor(s, m, "float32") for s in ("mean", "mean_eps", "rstd"))
+    steps = (
+        Kernel("x2=x*x", (x,), (sq,), m * n),
+        Kernel("mean=sum(x2)", (sq,), (mean,), m * n),
+        Kernel("+eps", (mean,), (mean_eps,), m),
+        Kernel("rsqrt", (mean_eps,), (rstd,), m),
+        Kernel("x*rstd", (x, rstd), (sc,), m * n),
+        Kernel("*w", (sc, w), (y,), m * n),
+    )
+    return Plan("RMSNorm, 6 eager steps", steps), Plan(
+        "RMSNorm, fused", (Kernel("rmsnorm", (x, w), (y,), 4 * m * n + 2 * m),)
+    )
+
+
+def _layernorm(m: int, n: int, dt: str):
+    x, g, b, y = Tensor("x", m * n, dt), Tensor("g", n, dt), Tensor("b", n, dt), Tensor("y", m * n, dt)
+    sq, acc = Tensor("x2", m * n, dt), Tensor("acc", m * n, dt)
+    sx, sx2 = Tensor("sum_x", m, "float32"), Tensor("sum_x2", m, "float32")
+    steps = (
+        Kernel("x2=x*x", (x,), (sq,), m * n),
+        Kernel("sum x", (x,), (sx,), m * n),
+        Kernel("sum x2", (sq,), (sx2,), m * n),
+        Kernel("x-mean", (x,), (acc,), m * n),
+        Kernel("*rstd", (acc,), (acc,), m * n),
+        Kernel("*g+b", (acc, g, b), (y,), 2 * m * n),
+    )
+    return Plan("LayerNorm, multi-pass", steps), Plan(
+        "LayerNorm, fused", (Kernel("layernorm", (x, g, b), (y,), 6 * m * n + 2 * m),)
+    )
+
+
+def _rope(tokens: int, heads: int, rope_dim: int, dt: str):
+    values = tokens * heads * rope_dim
+    pairs = values // 2
+    x, y = Tensor("x", values, dt), Tensor("y", values, dt)
+    rot, t, u = (Tensor(s, values, dt) for s in ("rot", "t", "u"))
+    cos_b, sin_b = Tensor("cos_b", values, dt), Tensor("sin_b", values, dt)
+    cos, sin = Tensor("cos", pairs, dt), Tensor("sin", pairs, dt)
+    steps = (
+        Kernel("rot=rotate_half(x)", (x,), (rot,), 0),
+        Kernel("t=x*cos", (x, cos_b), (t,), values),
+        Kernel("u=rot*sin", (rot, sin_b), (u,), values),
+        Kernel("y=t+u", (t, u), (y,), values),
+    )
+    return Plan("RoPE, 4 steps", steps), Plan("RoPE, fused", (Kernel("rope", (x, cos, sin), (y,), 3 * values),))
+
+
+def _norm_rope_quant(m: int, n: int, rope_dim: int, dt: str):
+    x, w = Tensor("x", m * n, dt), Tensor("w", n, dt)
+    cos, sin = Tensor("cos", m * rope_dim // 2, dt), Tensor("sin", m * rope_dim // 2, dt)
+    normed, rotated = Tensor("normed", m * n, dt), Tensor("rotated", m * n, dt)
+    q, amax = Tensor("q", m * n, "float8_e4m3fn"), Tensor("amax", m, "float32")
+    sep = (
+        Kernel("rmsnorm", (x, w), (normed,), 4 * m * n + 2 * m),
+        Kernel("rope", (normed, cos, sin), (rotated,), 3 * m * rope_dim),
+        Kernel("quant", (rotated,), (q, amax), 3 * m * n + m),
+    )
+    fused = Kernel("norm+rope+quant", (x, w, cos, sin), (q, amax), 4 * m * n + 3 * m * rope_dim + 3 * m * n + 3 * m)
+    return Plan("norm+rope+quant, 3 kernels", sep), Plan("norm+rope+quant, fused", (fused,))
+
+
+def p4_plans():
+    """The chapter-13 ledger's five (unfused, fused) pairs at that page's default sizes."""
+    return [
+        _scale_add(1 << 20, "float32"),
+        _rmsnorm(4096, 4096, "float16"),
+        _layernorm(4096, 4096, "bfloat16"),
+        _rope(4096, 32, 128, "float16"),
+        _norm_rope_quant(4096, 4096, 128, "bfloat16"),
+    ]
+
+
+# ----------------------------------------------------------- chapter 28 design model
+
+
+@dataclasses.dataclass(frozen=True)
+class QKShape:
+    tokens: int = 4096
+    q_heads: int = 32
+    kv_heads: int = 8
+    head_dim: int = 128
+    in_bytes: int = 2
+    out_bytes: int = 1
+    table_bytes: int = 4
+    on_chip_budget: int = 192 * 1024
+    sm_count: int = 132
+    blocks_per_sm: int = 8
+
+    @property
+    def rows(self) -> int:
+        return self.tokens * (self.q_heads + self.kv_heads)
+
+    @property
+    def elems(self) -> int:
+        return self.rows * self.head_dim
+
+
+def p3_flops(s: QKShape) -> int:
+    """Chapter-28 FLOP rule: norm 2D + 3 + 2D per row, RoPE 6 per pair, absmax D, quant 2D."""
+    d = s.head_dim
+    return s.rows * (2 * d + 3 + 2 * d + 6 * (d // 2) + d + 2 * d)
+
+
+def _p3_payload(s: QKShape) -> int:
+    return s.elems * (s.in_bytes + s.out_bytes) + s.rows * 4
+
+
+def _p3_weight_bytes(s: QKShape) -> int:
+    return 2 * s.head_dim * s.in_bytes  # q weight and k weight
+
+
+def _p3_table_bytes_per_token(s: QKShape) -> int:
+    return 2 * s.head_dim * s.table_bytes  # cos and sin as the page counts them
+
+
+def p3_ideal_bytes(s: QKShape) -> dict:
+    payload = _p3_payload(s)
+    lookup = _p3_weight_bytes(s) + s.tokens * _p3_table_bytes_per_token(s)
+    return {"payload": payload, "lookup": lookup, "total": payload + lookup}
+
+
+def p3_design(s: QKShape, name: str, rows_per_block: int, table_reads_per_token: float) -> dict:
+    grid = math.ceil(s.rows / rows_per_block)
+    lookup = grid * _p3_weight_bytes(s) + table_reads_per_token * s.tokens * _p3_table_bytes_per_token(s)
+    payload = _p3_payload(s)
+    d = s.head_dim
+    on_chip = rows_per_block * (d * s.in_bytes + d * s.out_bytes + d * 4 + 4) + 2 * d * s.table_bytes
+    resident = max(s.sm_count * s.blocks_per_sm, 1)
+    return {
+        "name": name,
+        "rows_per_block": rows_per_block,
+        "grid": grid,
+        "waves": math.ceil(grid / resident),
+        "on_chip": on_chip,
+        "payload": payload,
+        "lookup": lookup,
+        "total": payload + lookup,
+        "fits": on_chip <= s.on_chip_budget,
+    }
+
+
+def p3_designs(s: QKShape, rows_per_block_b: int = 8) -> list:
+    per_token = s.q_heads + s.kv_heads
+    return [
+        p3_design(s, "A: one row per block", 1, float(per_token)),
+        p3_design(s, f"B: {rows_per_block_b} rows per block", rows_per_block_b,
+                  float(math.ceil(per_token / rows_per_block_b))),
+        p3_design(s, "C: one whole token per block", per_token, 1.0),
+    ]
+
+
+# ----------------------------------------------- this library's algorithmic bytes
+
+
+def qk_bytes(tokens, q_heads, kv_heads, head_dim, rope_dim, in_bytes=2, write_y=False) -> dict:
+    """Bytes at the boundary of ``rnq_qk_norm_rope_fp8``: inputs read once, outputs written once,
+    weights once per call and the token's cos/sin row (fp32, rope_dim/2 wide) once per token."""
+    rows = tokens * (q_heads + kv_heads)
+    reads = rows * head_dim * in_bytes + 2 * tokens * (rope_dim // 2) * 4
+    reads += head_dim * in_bytes * ((q_heads > 0) + (kv_heads > 0))
+    writes = rows * head_dim + rows * 4 + (rows * head_dim * in_bytes if write_y else 0)
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
+def qk_flops(tokens, q_heads, kv_heads, head_dim, rope_dim) -> int:
+    """Chapter-28 rule with the RoPE term over rope_dim/2 pairs."""
+    rows = tokens * (q_heads + kv_heads)
+    d = head_dim
+    return rows * (2 * d + 3 + 2 * d + 6 * (rope_dim // 2) + d + 2 * d)
+
+
+def norm_rope_bytes(rows, width, rope_dim, rows_per_token=1, in_bytes=2) -> dict:
+    tables = rows // rows_per_token
+    reads = rows * width * in_bytes + width * in_bytes + 2 * tables * (rope_dim // 2) * 4
+    writes = rows * width * in_bytes
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
+def rmsnorm_fwd_bytes(rows, width, in_bytes=2, write_rstd=False) -> dict:
+    reads = rows * width * in_bytes + width * in_bytes
+    writes = rows * width * in_bytes + (rows * 4 if write_rstd else 0)
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
+def rmsnorm_bwd_bytes(rows, width, in_bytes=2, read_rstd=False) -> dict:
+    reads = 2 * rows * width * in_bytes + width * in_bytes + (rows * 4 if read_rstd else 0)
+    writes = rows * width * in_bytes + width * 4
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}

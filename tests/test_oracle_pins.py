@@ -1,0 +1,337 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+Each test ties one part of the oracle to something other than the oracle's
+own formula: a closed form, an identity of the rotation, a brute-force exact
+computation, a special case, or finite differences.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import codecs
+from oracle.exact import fraction_to_f32, sum_squares_exact_mask, sum_squares_f32
+
+F32 = np.float32
+
+
+def _bf16(x):
+    return codecs.bf16_round(np.asarray(x, np.float32))
+
+
+def _rows(M, N, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    return _bf16(rng.standard_normal((M, N)).astype(np.float32) * std)
+
+
+def _table(M, half, seed):
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(-np.pi, np.pi, (M, half))
+    return np.cos(ang).astype(F32), np.sin(ang).astype(F32)
+
+
+# ----------------------------------------------------------------- exact sum of squares
+
+
+def _brute_sumsq(row):
+    return fraction_to_f32(sum((Fraction(float(v)) ** 2 for v in row), Fraction(0)))
+
+
+def test_sum_squares_equals_exact_rational_rounding():
+    rng = np.random.default_rng(11)
+    rows = []
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        v = rng.standard_normal(n) * np.exp2(rng.integers(-60, 60, n))  # wide dynamic range
+        rows.append(codecs.bf16_to_f32(_bf16(v.astype(np.float32))))
+    for r in rows:
+        got = sum_squares_f32(r[None, :])[0]
+        assert got.tobytes() == _brute_sumsq(r).tobytes()
+
+
+def test_sum_squares_proof_flag_is_sound():
+    """Rows flagged exact really are: the float64 sum equals the rational sum."""
+    x = codecs.bf16_to_f32(_rows(300, 64, 12))
+    x[:100, 0] *= np.float32(2.0**-40)  # force some rows out of the proven range
+    s64, exact = sum_squares_exact_mask(x)
+    assert exact.sum() > 150 and (~exact).sum() > 0
+    for i in np.flatnonzero(exact)[:80]:
+        tot = sum((Fraction(float(v)) ** 2 for v in x[i]), Fraction(0))
+        assert Fraction(float(s64[i])) == tot
+
+
+def test_fraction_to_f32_matches_float_rounding():
+    rng = np.random.default_rng(13)
+    for _ in range(2000):
+        v = float(rng.standard_normal() * 2.0 ** rng.integers(-150, 120))
+        got = fraction_to_f32(Fraction(abs(v)))
+        assert got.tobytes() == np.float32(abs(v)).tobytes()  # a double is one exact rational
+    # ties to even at the fp32 grid: 1 + 2^-24 lies halfway between 1 and 1 + 2^-23
+    assert fraction_to_f32(Fraction(1) + Fraction(1, 1 << 24)) == np.float32(1.0)
+    assert fraction_to_f32(Fraction(1) + Fraction(3, 1 << 24)) == np.float32(1.0 + 2.0**-22)
+
+
+# ------------------------------------------------------------------------- RoPE pins
+
+
+def test_rope_identity_when_cos_one_sin_zero():
+    """cos = 1, sin = 0 leaves every nonzero value bit-identical.
+
+    Zeros keep their value but IEEE addition decides their sign: -0 - (hi * 0)
+    is +0 when hi < 0, so only the magnitude of a zero is pinned.
+    """
+    n = _rows(64, 128, 21)
+    n[0, 100] = 0x8000
+    n[1, 70] = 0x0000
+    for half in (8, 32, 64):
+        c = np.ones((64, half), F32)
+        s = np.zeros((64, half), F32)
+        y = oracle.rope_tail(n, c, s)
+        nz = (n & 0x7FFF) != 0
+        assert np.array_equal(y[nz], n[nz])
+        assert np.all((y[~nz] & 0x7FFF) == 0)
+
+
+def test_rope_preserves_pair_norm_in_exact_arithmetic():
+    x = _rows(32, 128, 22)
+    w = _bf16(1 + 0.1 * np.random.default_rng(23).standard_normal(128))
+    c, s = _table(32, 32, 24)
+    y = oracle.truth_norm_rope(x, w, c, s, 1e-6)
+    n = oracle.truth_norm_rope(x, w, np.zeros((32, 0)), np.zeros((32, 0)), 1e-6)
+    lo, hi = n[:, 64:96], n[:, 96:]
+    ylo, yhi = y[:, 64:96], y[:, 96:]
+    lhs = ylo**2 + yhi**2
+    rhs = (lo**2 + hi**2) * (c.astype(np.float64) ** 2 + s.astype(np.float64) ** 2)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=0)
+    assert np.array_equal(y[:, :64], n[:, :64])  # columns outside the rope tail pass through
+
+
+def test_rope_is_the_complex_product():
+    x = _rows(16, 64, 25)
+    w = _bf16(np.ones(64))
+    c, s = _table(16, 32, 26)
+    y = oracle.truth_norm_rope(x, w, c, s, 1e-6)
+    n = oracle.truth_norm_rope(x, w, np.zeros((16, 0)), np.zeros((16, 0)), 1e-6)
+    z = (n[:, :32] + 1j * n[:, 32:]) * (c.astype(np.float64) + 1j * s.astype(np.float64))
+    np.testing.assert_allclose(y[:, :32], z.real, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(y[:, 32:], z.imag, rtol=0, atol=1e-14)
+
+
+def test_rope_pairs_p_with_p_plus_half_of_the_tail():
+    """NeoX half split on the last R columns: a unit at tail column p rotates into p + R/2."""
+    N, R = 32, 16
+    n = np.zeros((1, N), np.uint16)
+    n[0, N - R + 3] = _bf16(1.0)
+    c = np.zeros((1, R // 2), F32)
+    s = np.ones((1, R // 2), F32)  # rotation by +90 degrees
+    y = codecs.bf16_to_f32(oracle.rope_tail(n, c, s))
+    expect = np.zeros(N, F32)
+    expect[N - R // 2 + 3] = 1.0
+    assert np.array_equal(y[0], expect)
+
+
+# ---------------------------------------------------------------------- RMSNorm pins
+
+
+@pytest.mark.parametrize("a", [1.0, -1.0, 0.5, -0.5, 3.0, -3.0])
+def test_constant_row_normalises_to_plus_minus_w(a):
+    rng = np.random.default_rng(31)
+    w = _bf16(rng.standard_normal(256))
+    x = _bf16(np.full((4, 256), a, np.float32))
+    y, _ = oracle.rmsnorm_fwd(x, w, 1e-6)
+    expect = _bf16(np.sign(a) * codecs.bf16_to_f32(w))
+    assert np.array_equal(y, np.broadcast_to(expect, y.shape))
+
+
+def test_m32_within_one_bf16_ulp_of_float64():
+    x = _rows(256, 128, 32)
+    w = _bf16(1 + 0.1 * np.random.default_rng(33).standard_normal(128))
+    c, s = _table(256, 32, 34)
+    y32, _, _ = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 448.0)
+    y64 = oracle.truth_norm_rope(x, w, c, s, 1e-6, round_intermediates=True)
+    # distance in bf16 steps between the oracle's y and the float64 composition
+    y64b = codecs.bf16_round(y64.astype(np.float32))
+    d = np.abs(y32.astype(np.int32) - y64b.astype(np.int32))
+    same_sign = (y32 & 0x8000) == (y64b & 0x8000)
+    assert np.all(d[same_sign] <= 1)
+    assert np.mean(d == 0) > 0.999
+
+
+def test_zero_row():
+    w = _bf16(np.array([1.0, -2.0] * 64, np.float32))
+    x = np.zeros((3, 128), np.uint16)
+    c, s = _table(3, 32, 35)
+    y, codes, scale = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 448.0)
+    assert np.all(codecs.bf16_to_f32(y) == 0)
+    # sign of zero: +0 * w keeps w's sign outside the tail
+    assert np.array_equal(codes[:, :64] & 0x80, np.where(codecs.bf16_to_f32(w[:64]) < 0, 0x80, 0)[None, :].repeat(3, 0))
+    assert np.all((codes & 0x7F) == 0)
+    assert np.all(scale == fraction_to_f32(Fraction(float(np.float32(1e-4))) / 448))
+
+
+# ----------------------------------------------------------------- quantisation pins
+
+
+def _exact_div_f32(a, b):
+    return fraction_to_f32(Fraction(float(a)) / Fraction(float(b)))
+
+
+def test_scale_is_correctly_rounded_amax_over_fp8_max():
+    x = _rows(200, 128, 41)
+    x[:5] = _bf16(codecs.bf16_to_f32(x[:5]) * 1e-7)  # rows below the 1e-4 floor
+    w = _bf16(1 + 0.1 * np.random.default_rng(42).standard_normal(128))
+    c, s = _table(200, 32, 43)
+    for fp8_max in (448.0, 240.0, 57.0):
+        y, codes, scale = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, fp8_max)
+        amax = np.abs(codecs.bf16_to_f32(y)).max(axis=1)
+        for i in range(200):
+            a = max(float(amax[i]), float(np.float32(1e-4)))
+            assert scale[i].tobytes() == _exact_div_f32(a, fp8_max).tobytes()
+
+
+def test_max_code_is_448_for_rows_above_the_floor():
+    d_in = _rows(500, 128, 44)
+    w = _bf16(1 + 0.1 * np.random.default_rng(45).standard_normal(128))
+    c, s = _table(500, 32, 46)
+    y, codes, scale = oracle.norm_rope_quant_rows(d_in, w, c, s, 1e-6, 448.0)
+    mag = codes & 0x7F
+    assert np.all(mag.max(axis=1) == 0x7E)
+    assert not np.any(mag == 0x7F)  # NaN never produced
+
+
+def test_codes_decode_back_within_e4m3_rounding():
+    x = _rows(300, 128, 47)
+    w = _bf16(1 + 0.1 * np.random.default_rng(48).standard_normal(128))
+    c, s = _table(300, 64, 49)
+    y, codes, scale = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 448.0)
+    yv = codecs.bf16_to_f32(y).astype(np.float64)
+    dec = codecs.e4m3_decode(codes).astype(np.float64) * scale[:, None].astype(np.float64)
+    err = np.abs(dec - yv)
+    q = np.abs(yv) / scale[:, None]
+    normal = q >= 2.0**-6
+    slack = 1e-6 * np.abs(yv) + 1e-30
+    assert np.all(err[normal] <= 2.0**-4 * np.abs(yv[normal]) + slack[normal])
+    sub_bound = 2.0**-10 * scale[:, None].astype(np.float64) * (1 + 1e-6)
+    assert np.all(err[~normal] <= np.broadcast_to(sub_bound, err.shape)[~normal])
+
+
+def test_clamp_applies_for_smaller_fp8_max():
+    x = _rows(64, 128, 50)
+    w = _bf16(np.ones(128))
+    c, s = _table(64, 64, 51)
+    _, codes, _ = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 240.0)
+    lim = int(codecs.e4m3_encode(np.float32(240.0)))
+    assert (codes & 0x7F).max() == lim
+
+
+def test_qk_shares_the_token_row_across_heads():
+    """Every head of a token is rotated by that token's table row."""
+    T, Hq, Hk, D = 5, 3, 2, 64
+    rng = np.random.default_rng(52)
+    q = _bf16(rng.standard_normal((T, Hq, D)))
+    k = _bf16(rng.standard_normal((T, Hk, D)))
+    wq = _bf16(1 + 0.1 * rng.standard_normal(D))
+    wk = _bf16(1 + 0.1 * rng.standard_normal(D))
+    c, s = _table(T, D // 2, 53)
+    out = oracle.qk_norm_rope_fp8(q, k, wq, wk, c, s)
+    for t in range(T):
+        for h in range(Hk):
+            y, codes, scale = oracle.norm_rope_quant_rows(k[t, h][None], wk, c[t][None], s[t][None], 1e-6, 448.0)
+            assert np.array_equal(out["k_codes"][t, h], codes[0])
+            assert out["k_scale"][t, h] == scale[0]
+
+
+# -------------------------------------------------------------------- backward pins
+
+
+def _loss_exact(x, w, gy, eps):
+    ms = (x * x).mean(axis=-1)
+    rstd = 1.0 / np.sqrt(ms + eps)
+    return float((gy * x * rstd[:, None] * w[None, :]).sum())
+
+
+def test_backward_matches_central_differences():
+    rng = np.random.default_rng(61)
+    M, N = 3, 12
+    eps = float(np.float32(1e-6))
+    xb = _bf16(rng.standard_normal((M, N)))
+    wb = _bf16(rng.standard_normal(N))
+    gb = _bf16(rng.standard_normal((M, N)))
+    dx, dw, _ = oracle.rmsnorm_bwd(xb, wb, gb, 1e-6)
+    x = codecs.bf16_to_f32(xb).astype(np.float64)
+    w = codecs.bf16_to_f32(wb).astype(np.float64)
+    g = codecs.bf16_to_f32(gb).astype(np.float64)
+    h = 1e-6
+    fd_x = np.zeros_like(x)
+    for i in range(M):
+        for j in range(N):
+            xp = x.copy(); xp[i, j] += h
+            xm = x.copy(); xm[i, j] -= h
+            fd_x[i, j] = (_loss_exact(xp, w, g, eps) - _loss_exact(xm, w, g, eps)) / (2 * h)
+    fd_w = np.zeros_like(w)
+    for j in range(N):
+        wp = w.copy(); wp[j] += h
+        wm = w.copy(); wm[j] -= h
+        fd_w[j] = (_loss_exact(x, wp, g, eps) - _loss_exact(x, wm, g, eps)) / (2 * h)
+    np.testing.assert_allclose(dx, fd_x, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dw, fd_w, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_backward_scale_invariance_identity(eps):
+    """sum_j x_j dx_j = N * C * eps * rstd^2 per row (zero when eps = 0)."""
+    rng = np.random.default_rng(62)
+    M, N = 8, 96
+    xb = _bf16(rng.standard_normal((M, N)))
+    wb = _bf16(rng.standard_normal(N))
+    gb = _bf16(rng.standard_normal((M, N)))
+    dx, _, rstd = oracle.rmsnorm_bwd(xb, wb, gb, eps)
+    x = codecs.bf16_to_f32(xb).astype(np.float64)
+    w = codecs.bf16_to_f32(wb).astype(np.float64)
+    g = codecs.bf16_to_f32(gb).astype(np.float64) * w
+    xn = x * rstd[:, None]
+    C = (g * xn).mean(axis=1)
+    lhs = (x * dx).sum(axis=1)
+    rhs = N * C * float(np.float32(eps)) * rstd**2
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-9, atol=1e-11 * np.abs(x * dx).sum(axis=1).max())
+
+
+def test_backward_single_row_dw():
+    rng = np.random.default_rng(63)
+    xb = _bf16(rng.standard_normal((1, 40)))
+    wb = _bf16(rng.standard_normal(40))
+    gb = _bf16(rng.standard_normal((1, 40)))
+    _, dw, rstd = oracle.rmsnorm_bwd(xb, wb, gb, 1e-6)
+    x = codecs.bf16_to_f32(xb[0]).astype(np.float64)
+    g = codecs.bf16_to_f32(gb[0]).astype(np.float64)
+    np.testing.assert_allclose(dw, g * x * rstd[0], rtol=1e-15)
+
+
+# ----------------------------------------------------- consistency with the pages' torch code
+
+
+def test_agrees_with_torch_reference_up_to_summation_order():
+    """The pages' torch reference sums squares in torch's own order; results agree to 1 ulp.
+
+    Not a pin (it shares the formula); it shows what the exact-sum reading changes.
+    """
+    rng = np.random.default_rng(71)
+    M, N, half = 2048, 128, 32
+    x = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((1 + 0.1 * rng.standard_normal(N)).astype(np.float32)).to(torch.bfloat16)
+    c, s = _table(M, half, 72)
+    cos, sin = torch.from_numpy(c), torch.from_numpy(s)
+    rstd = torch.rsqrt(x.float().pow(2).mean(-1, keepdim=True) + 1e-6)
+    normed = (x.float() * rstd * w.float().unsqueeze(0)).to(x.dtype)
+    R = 2 * half
+    lo, hi = normed[:, -R:].float()[:, :half], normed[:, -R:].float()[:, half:]
+    y = torch.cat([normed[:, :-R], torch.cat([lo * cos - hi * sin, hi * cos + lo * sin], -1).to(x.dtype)], -1)
+    yb = y.view(torch.int16).numpy().view(np.uint16)
+    ours, _, _ = oracle.norm_rope_quant_rows(x.view(torch.int16).numpy().view(np.uint16),
+                                             w.view(torch.int16).numpy().view(np.uint16), c, s, 1e-6, 448.0)
+    d = np.abs(ours.astype(np.int32) - yb.astype(np.int32))
+    assert np.all(d <= 1)
+    assert np.mean(d == 0) > 0.9995

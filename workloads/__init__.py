@@ -1,0 +1,193 @@
+"""Seeded synthetic inputs for the RMSNorm -> partial NeoX RoPE -> FP8 prologue.
+
+This module is shared by the HIP path (tests, bench) and by the CPU oracle. It
+holds no arithmetic of the method itself: it only draws random numbers, rounds
+them to the input dtype, and builds the cos/sin table that the method takes as
+an input. Everything is generated on the host with ``torch.Generator("cpu")``
+so that both sides see identical bytes.
+
+Workloads (sizes follow the tutorial pages' problem statement: rows ``[M, N]``
+where M = tokens x heads, weight ``[N]``, cos/sin ``[tokens, rope_dim/2]``):
+
+* ``qk_small``   - 256 rows x 128, rope 64, bf16, one cos/sin row per row (pos = row)
+* ``rmsnorm_4k`` - 4096 x 4096 bf16, RMSNorm forward and backward
+* ``norm_rope_fp16`` - 16384 rows x 128, rope 64, fp16 x = 2*N(0,1), random positions
+* ``qk_4k``      - 4096 tokens x (32 q + 8 kv) heads x 128, full rope, 1% outliers x20
+* ``qk_64k``     - 65536 tokens x (64 q + 8 kv) heads x 128, full rope, theta = 1e6
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+
+import numpy as np
+import torch
+
+__all__ = [
+    "WORKLOADS",
+    "Workload",
+    "generate",
+    "rope_table",
+    "bits",
+    "sha256",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "qk" (norm+rope+fp8), "norm_rope", "rmsnorm"
+    seed: int
+    tokens: int = 0
+    q_heads: int = 0
+    kv_heads: int = 0
+    head_dim: int = 0
+    rope_dim: int = 0
+    rows: int = 0  # for rmsnorm / norm_rope: M
+    width: int = 0  # for rmsnorm / norm_rope: N
+    dtype: str = "bf16"
+    theta: float = 10000.0
+    eps: float = 1e-6
+    fp8_max: float = 448.0
+    outlier_p: float = 0.0
+    outlier_mul: float = 20.0
+    write_y: bool = False
+    x_std: float = 1.0
+    positions: str = "index"  # "index" (pos = token/row index) or "random:<hi>"
+    description: str = ""
+
+
+WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload(
+            "qk_small", "qk", seed=1001, tokens=256, q_heads=1, kv_heads=0, head_dim=128,
+            rope_dim=64, write_y=True,
+            description="fused RMSNorm + partial RoPE + FP8, 256 rows x 128, rope 64, bf16, y written",
+        ),
+        Workload(
+            "rmsnorm_4k", "rmsnorm", seed=1002, rows=4096, width=4096,
+            description="RMSNorm forward + backward, 4096 x 4096 bf16",
+        ),
+        Workload(
+            "norm_rope_fp16", "norm_rope", seed=1003, rows=16384, width=128, rope_dim=64,
+            dtype="fp16", x_std=2.0, positions="random:8192",
+            description="RMSNorm + partial RoPE (no quant), 16384 x 128, rope 64, fp16",
+        ),
+        Workload(
+            "qk_4k", "qk", seed=1004, tokens=4096, q_heads=32, kv_heads=8, head_dim=128,
+            rope_dim=128, outlier_p=0.01,
+            description="QK-norm + RoPE + FP8, 4096 tokens x (32+8) heads x 128, bf16",
+        ),
+        Workload(
+            "qk_64k", "qk", seed=1005, tokens=65536, q_heads=64, kv_heads=8, head_dim=128,
+            rope_dim=128, theta=1e6,
+            description="QK-norm + RoPE + FP8, 65536 tokens x (64+8) heads x 128, bf16, theta 1e6",
+        ),
+    ]
+}
+
+_TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def rope_table(positions: np.ndarray, rope_dim: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin tables ``[len(positions), rope_dim/2]`` fp32.
+
+    The pages take cos/sin as inputs and do not say how they are made; the
+    usual NeoX convention is used: frequency i is theta^(-2i/rope_dim), the
+    angle is position x frequency. Angles and cos/sin are evaluated in fp64
+    and rounded to fp32 once.
+    """
+    half = rope_dim // 2
+    pos = np.asarray(positions, dtype=np.float64)
+    if half == 0:
+        z = np.zeros((pos.shape[0], 0), dtype=np.float32)
+        return z, z.copy()
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / rope_dim)
+    ang = pos[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _positions(spec: str, n: int, g: torch.Generator) -> np.ndarray:
+    if spec == "index":
+        return np.arange(n, dtype=np.int64)
+    kind, hi = spec.split(":")
+    assert kind == "random"
+    return torch.randint(0, int(hi), (n,), generator=g).numpy().astype(np.int64)
+
+
+def _normal(shape, g, std=1.0):
+    return torch.randn(*shape, generator=g, dtype=torch.float32) * std
+
+
+def _with_outliers(x: torch.Tensor, g: torch.Generator, p: float, mul: float) -> torch.Tensor:
+    if p <= 0:
+        return x
+    mask = torch.rand(x.shape, generator=g) < p
+    return torch.where(mask, x * mul, x)
+
+
+def generate(name_or_wl, *, tokens: int | None = None, seed: int | None = None) -> dict:
+    """Build the inputs of a workload on the host.
+
+    ``tokens`` (qk) or rows (others) may be overridden to build a smaller
+    instance of the same recipe. Returned tensors are CPU tensors in the
+    workload dtype; cos/sin are fp32 numpy arrays wrapped as tensors.
+    """
+    wl = WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
+    g = torch.Generator("cpu").manual_seed(wl.seed if seed is None else seed)
+    dt = _TORCH_DT[wl.dtype]
+    out: dict = {"workload": wl}
+    if wl.kind == "qk":
+        T = wl.tokens if tokens is None else tokens
+        D, Hq, Hk = wl.head_dim, wl.q_heads, wl.kv_heads
+        q = _with_outliers(_normal((T, Hq, D), g, wl.x_std), g, wl.outlier_p, wl.outlier_mul)
+        k = _with_outliers(_normal((T, Hk, D), g, wl.x_std), g, wl.outlier_p, wl.outlier_mul)
+        wq = 1.0 + 0.1 * _normal((D,), g)
+        wk = 1.0 + 0.1 * _normal((D,), g)
+        pos = _positions(wl.positions, T, g)
+        cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
+        out.update(
+            q=q.to(dt), k=k.to(dt), wq=wq.to(dt), wk=wk.to(dt),
+            cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
+            tokens=T, q_heads=Hq, kv_heads=Hk, head_dim=D, rope_dim=wl.rope_dim,
+        )
+    elif wl.kind == "norm_rope":
+        M = wl.rows if tokens is None else tokens
+        N = wl.width
+        x = _normal((M, N), g, wl.x_std)
+        w = 1.0 + 0.1 * _normal((N,), g)
+        pos = _positions(wl.positions, M, g)
+        cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
+        out.update(
+            x=x.to(dt), w=w.to(dt), cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
+            rows=M, width=N, rope_dim=wl.rope_dim, rows_per_token=1,
+        )
+    elif wl.kind == "rmsnorm":
+        M = wl.rows if tokens is None else tokens
+        N = wl.width
+        x = _normal((M, N), g, wl.x_std)
+        w = _normal((N,), g)
+        gy = _normal((M, N), g)
+        out.update(x=x.to(dt), w=w.to(dt), grad_y=gy.to(dt), rows=M, width=N)
+    else:  # pragma: no cover
+        raise ValueError(wl.kind)
+    return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a 16-bit float tensor as uint16 (a reinterpretation, no rounding)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return t.view(torch.uint8).numpy()
+    raise TypeError(t.dtype)
+
+
+def sha256(t) -> str:
+    a = t if isinstance(t, np.ndarray) else bits(t)
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
