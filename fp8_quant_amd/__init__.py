@@ -1,0 +1,286 @@
+"""fp8_quant_amd: RMSNorm -> partial NeoX RoPE -> per-row FP8 e4m3fn on MI355X.
+
+Python binding of ``librnq.so`` (C ABI declared in ``include/rnq.h``). The
+functions named ``rnq_*`` mirror the C entry points one to one: they take
+torch tensors that live on the GPU, check shapes and dtypes, and pass raw
+pointers, sizes and torch's current stream through ctypes. Every step of the
+computation runs in the HIP kernels; there is no CPU path. If the library has
+not been built, the first call raises.
+
+Convenience wrappers (``qk_norm_rope_fp8``, ``rmsnorm``, ``rmsnorm_bwd``,
+``rmsnorm_rope``) allocate the outputs with torch and call the same entry
+points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "RnqError",
+    "library_path",
+    "load_library",
+    "rnq_status_string",
+    "rnq_abi_version",
+    "rnq_qk_norm_rope_fp8",
+    "rnq_rmsnorm_rope",
+    "rnq_rmsnorm_fwd",
+    "rnq_rmsnorm_bwd",
+    "rnq_rmsnorm_bwd_workspace_size",
+    "qk_norm_rope_fp8",
+    "rmsnorm",
+    "rmsnorm_bwd",
+    "rmsnorm_rope",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+EXPORTED_SYMBOLS = (
+    "rnq_status_string",
+    "rnq_last_error",
+    "rnq_abi_version",
+    "rnq_rmsnorm_fwd",
+    "rnq_rmsnorm_bwd_workspace_size",
+    "rnq_rmsnorm_bwd",
+    "rnq_rmsnorm_rope",
+    "rnq_qk_norm_rope_fp8",
+)
+
+RNQ_BF16 = 0
+RNQ_F16 = 1
+
+
+class RnqError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}" if detail else name)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("RNQ_LIBRARY", os.path.join(_HERE, "librnq.so"))
+
+
+def load_library():
+    """Load librnq.so once; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not built: {path} is missing (run `python -m fp8_quant_amd.build`)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.rnq_status_string.argtypes = [i32]
+    lib.rnq_status_string.restype = ctypes.c_char_p
+    lib.rnq_last_error.argtypes = []
+    lib.rnq_last_error.restype = ctypes.c_char_p
+    lib.rnq_abi_version.argtypes = []
+    lib.rnq_abi_version.restype = i32
+    lib.rnq_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    lib.rnq_rmsnorm_fwd.restype = i32
+    lib.rnq_rmsnorm_bwd_workspace_size.argtypes = [i64, i64]
+    lib.rnq_rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.rnq_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, f32, i32, vp]
+    lib.rnq_rmsnorm_bwd.restype = i32
+    lib.rnq_rmsnorm_rope.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp]
+    lib.rnq_rmsnorm_rope.restype = i32
+    lib.rnq_qk_norm_rope_fp8.argtypes = [vp] * 12 + [i64] * 5 + [f32, f32, i32, vp]
+    lib.rnq_qk_norm_rope_fp8.restype = i32
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor on {t.device}: the rnq kernels need GPU tensors (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RNQ_BF16
+    if t.dtype == torch.float16:
+        return RNQ_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp16)")
+
+
+def _stream(t, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        name = lib.rnq_status_string(status).decode()
+        detail = lib.rnq_last_error().decode()
+        raise RnqError(status, name, detail)
+
+
+def _expect(t, dtype, shape, what):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ------------------------------------------------------------- C entry points
+
+
+def rnq_status_string(status: int) -> str:
+    return load_library().rnq_status_string(status).decode()
+
+
+def rnq_abi_version() -> int:
+    return load_library().rnq_abi_version()
+
+
+def rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None,
+                         *, eps: float = 1e-6, fp8_max: float = 448.0, stream=None) -> None:
+    """QK-norm + RoPE + FP8 into caller-provided outputs (see include/rnq.h)."""
+    torch = _torch()
+    lib = load_library()
+    T, Hq, D = q.shape
+    Hk = 0 if k is None else k.shape[1]
+    half = 0 if cos is None else cos.shape[-1]
+    dt = q.dtype
+    if k is not None:
+        _expect(k, dt, (T, Hk, D), "k")
+    _expect(wq, dt, (D,), "wq")
+    _expect(wk, dt, (D,), "wk")
+    if cos is not None:
+        _expect(cos, torch.float32, (T, half), "cos")
+        _expect(sin, torch.float32, (T, half), "sin")
+    for o, H, nm in ((q_fp8, Hq, "q_fp8"), (k_fp8, Hk, "k_fp8")):
+        if o is not None and o.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{nm}: expected uint8 or float8_e4m3fn")
+        if o is not None and tuple(o.shape) != (T, H, D):
+            raise ValueError(f"{nm}: shape {tuple(o.shape)}, expected {(T, H, D)}")
+    _expect(q_scale, torch.float32, (T, Hq), "q_scale")
+    _expect(k_scale, torch.float32, (T, Hk), "k_scale")
+    _expect(q_y, dt, (T, Hq, D), "q_y")
+    _expect(k_y, dt, (T, Hk, D), "k_y")
+    status = lib.rnq_qk_norm_rope_fp8(
+        _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(cos), _ptr(sin),
+        _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale), _ptr(k_scale), _ptr(q_y), _ptr(k_y),
+        T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
+    )
+    _check(status)
+
+
+def rnq_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float = 1e-6, stream=None) -> None:
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    half = 0 if cos is None else cos.shape[-1]
+    _expect(w, x.dtype, (N,), "w")
+    _expect(y, x.dtype, (M, N), "y")
+    if cos is not None:
+        _expect(cos, torch.float32, (M // max(rows_per_token, 1), half), "cos")
+        _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
+    status = lib.rnq_rmsnorm_rope(_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), M, N, 2 * half,
+                                  rows_per_token, eps, _dtype_code(x), _stream(x, stream))
+    _check(status)
+
+
+def rnq_rmsnorm_fwd(x, w, y, rstd=None, *, eps: float = 1e-6, stream=None) -> None:
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    _expect(w, x.dtype, (N,), "w")
+    _expect(y, x.dtype, (M, N), "y")
+    _expect(rstd, torch.float32, (M,), "rstd")
+    status = lib.rnq_rmsnorm_fwd(_ptr(x), _ptr(w), _ptr(y), _ptr(rstd), M, N, eps, _dtype_code(x), _stream(x, stream))
+    _check(status)
+
+
+def rnq_rmsnorm_bwd_workspace_size(M: int, N: int) -> int:
+    return int(load_library().rnq_rmsnorm_bwd_workspace_size(M, N))
+
+
+def rnq_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, eps: float = 1e-6, stream=None) -> None:
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    _expect(w, x.dtype, (N,), "w")
+    _expect(grad_y, x.dtype, (M, N), "grad_y")
+    _expect(grad_x, x.dtype, (M, N), "grad_x")
+    _expect(grad_w, torch.float32, (N,), "grad_w")
+    _expect(rstd, torch.float32, (M,), "rstd")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib.rnq_rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(grad_y), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
+                                 _ptr(workspace), ws_bytes, M, N, eps, _dtype_code(x), _stream(x, stream))
+    _check(status)
+
+
+# ------------------------------------------------------- allocating wrappers
+
+
+def qk_norm_rope_fp8(q, k, wq, wk, cos, sin, *, eps=1e-6, fp8_max=448.0, return_y=False):
+    """Returns (q8, k8, q_scale, k_scale[, q_y, k_y]); codes as torch.float8_e4m3fn."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    Hk = 0 if k is None else k.shape[1]
+    dev = q.device
+    q8 = torch.empty((T, Hq, D), dtype=torch.uint8, device=dev)
+    k8 = torch.empty((T, Hk, D), dtype=torch.uint8, device=dev)
+    qs = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    ks = torch.empty((T, Hk), dtype=torch.float32, device=dev)
+    qy = torch.empty_like(q) if return_y else None
+    ky = (torch.empty_like(k) if k is not None else None) if return_y else None
+    rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q8, k8 if Hk else None, qs, ks if Hk else None, qy, ky,
+                         eps=eps, fp8_max=fp8_max)
+    out = (q8.view(torch.float8_e4m3fn), k8.view(torch.float8_e4m3fn), qs, ks)
+    return out + (qy, ky) if return_y else out
+
+
+def rmsnorm(x, w, *, eps=1e-6, return_rstd=False):
+    torch = _torch()
+    y = torch.empty_like(x)
+    rstd = torch.empty((x.shape[0],), dtype=torch.float32, device=x.device) if return_rstd else None
+    rnq_rmsnorm_fwd(x, w, y, rstd, eps=eps)
+    return (y, rstd) if return_rstd else y
+
+
+def rmsnorm_bwd(x, w, grad_y, rstd=None, *, eps=1e-6):
+    """Returns (grad_x, grad_w fp32)."""
+    torch = _torch()
+    M, N = x.shape
+    gx = torch.empty_like(x)
+    gw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    ws = torch.empty((max(rnq_rmsnorm_bwd_workspace_size(M, N), 16) // 4,), dtype=torch.float32, device=x.device)
+    rnq_rmsnorm_bwd(x, w, grad_y, gx, gw, ws, rstd, eps=eps)
+    return gx, gw
+
+
+def rmsnorm_rope(x, w, cos, sin, *, rows_per_token=1, eps=1e-6):
+    torch = _torch()
+    y = torch.empty_like(x)
+    rnq_rmsnorm_rope(x, w, cos, sin, y, rows_per_token=rows_per_token, eps=eps)
+    return y

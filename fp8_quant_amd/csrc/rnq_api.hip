@@ -1,0 +1,270 @@
+// C ABI of librnq.so: argument validation and dispatch to the HIP kernels.
+// The contract of every entry point is documented in include/rnq.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "rnq.h"
+#include "rnq_launch.h"
+
+namespace rnq {
+
+static thread_local std::string g_last_error;
+
+static rnq_status fail(rnq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static rnq_status fail(rnq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+static rnq_status ok() {
+  g_last_error.clear();
+  return RNQ_OK;
+}
+
+static rnq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RNQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static uint32_t env_u32(const char* name, uint32_t dflt) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == 0) return dflt;
+  long x = strtol(v, nullptr, 10);
+  return x > 0 ? (uint32_t)x : dflt;
+}
+
+uint32_t tuning_target_waves() {
+  static const uint32_t v = env_u32("RNQ_TARGET_WAVES", 4096);
+  return v;
+}
+
+uint32_t tuning_passes_per_wave() {
+  static const uint32_t v = env_u32("RNQ_PASSES_PER_WAVE", 0);
+  return v;
+}
+
+static bool row_width_ok(int64_t n) { return n == 64 || n == 128 || n == 256 || n == 512; }
+
+static rnq_status check_eps(float eps) {
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(RNQ_ERR_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+  return RNQ_OK;
+}
+
+static rnq_status check_dtype(int dtype) {
+  if (dtype != RNQ_BF16 && dtype != RNQ_F16) return fail(RNQ_ERR_ARG, "unknown dtype %d", dtype);
+  return RNQ_OK;
+}
+
+// rope_dim rules: even and <= width (the pages' checks), and a multiple of 16
+// (both halves of the tail split into whole 16-byte chunks)
+static rnq_status check_rope(int64_t rope_dim, int64_t width) {
+  if (rope_dim < 0 || rope_dim % 2 != 0) return fail(RNQ_ERR_SHAPE, "rope_dim must be even and >= 0 (got %lld)", (long long)rope_dim);
+  if (rope_dim > width) return fail(RNQ_ERR_SHAPE, "rope_dim %lld exceeds the row width %lld", (long long)rope_dim, (long long)width);
+  if (rope_dim % 16 != 0) return fail(RNQ_ERR_UNSUPPORTED, "rope_dim must be a multiple of 16 (got %lld)", (long long)rope_dim);
+  return RNQ_OK;
+}
+
+}  // namespace rnq
+
+using namespace rnq;
+
+extern "C" {
+
+const char* rnq_status_string(int status) {
+  switch (status) {
+    case RNQ_OK: return "RNQ_OK";
+    case RNQ_ERR_NULL: return "RNQ_ERR_NULL: a required pointer is NULL";
+    case RNQ_ERR_SHAPE: return "RNQ_ERR_SHAPE: invalid shape";
+    case RNQ_ERR_UNSUPPORTED: return "RNQ_ERR_UNSUPPORTED: width or alignment not supported";
+    case RNQ_ERR_ARG: return "RNQ_ERR_ARG: invalid scalar argument";
+    case RNQ_ERR_WORKSPACE: return "RNQ_ERR_WORKSPACE: workspace too small";
+    case RNQ_ERR_HIP: return "RNQ_ERR_HIP: HIP runtime error";
+    default: return "RNQ_ERR_UNKNOWN";
+  }
+}
+
+const char* rnq_last_error(void) { return g_last_error.c_str(); }
+
+int rnq_abi_version(void) { return 100; }
+
+rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, const void* wk,
+                                const float* cos, const float* sin,
+                                uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                void* q_y, void* k_y,
+                                int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, int64_t rope_dim,
+                                float eps, float fp8_max, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (tokens < 0 || q_heads < 0 || kv_heads < 0 || head_dim < 0)
+    return fail(RNQ_ERR_SHAPE, "negative size (tokens %lld, q_heads %lld, kv_heads %lld, head_dim %lld)",
+                (long long)tokens, (long long)q_heads, (long long)kv_heads, (long long)head_dim);
+  if ((s = check_rope(rope_dim, head_dim)) != RNQ_OK) return s;
+  if (!row_width_ok(head_dim)) return fail(RNQ_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512 (got %lld)", (long long)head_dim);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
+  const int64_t heads = q_heads + kv_heads;
+  if (heads > 0 && tokens > ((int64_t)1 << 31) / heads)
+    return fail(RNQ_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31");
+  const int64_t rows = tokens * heads;
+  if (rows == 0) return ok();
+  if (q_heads > 0 && (!q || !wq || !q_fp8 || !q_scale)) return fail(RNQ_ERR_NULL, "q, wq, q_fp8 and q_scale are required when q_heads > 0");
+  if (kv_heads > 0 && (!k || !wk || !k_fp8 || !k_scale)) return fail(RNQ_ERR_NULL, "k, wk, k_fp8 and k_scale are required when kv_heads > 0");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
+  const void* a16[] = {q, k, wq, wk, cos, sin, q_y, k_y};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(q_fp8, 8) || !aligned(k_fp8, 8)) return fail(RNQ_ERR_UNSUPPORTED, "fp8 outputs must be 8-byte aligned");
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4)) return fail(RNQ_ERR_UNSUPPORTED, "scale outputs must be 4-byte aligned");
+
+  RowParams p = {};
+  const bool q_first = q_heads > 0;  // tensor 0 is q unless there are no q heads
+  p.x0 = (const uint16_t*)(q_first ? q : k);
+  p.w0 = (const uint16_t*)(q_first ? wq : wk);
+  p.c0 = q_first ? q_fp8 : k_fp8;
+  p.s0 = q_first ? q_scale : k_scale;
+  p.y0 = (uint16_t*)(q_first ? q_y : k_y);
+  p.x1 = (const uint16_t*)(q_first ? k : nullptr);
+  p.w1 = (const uint16_t*)(q_first ? wk : nullptr);
+  p.c1 = q_first ? k_fp8 : nullptr;
+  p.s1 = q_first ? k_scale : nullptr;
+  p.y1 = (uint16_t*)(q_first ? k_y : nullptr);
+  p.cos = cos;
+  p.sin = sin;
+  p.rstd = nullptr;
+  p.total_rows = (uint32_t)rows;
+  p.heads = (uint32_t)heads;
+  p.heads0 = (uint32_t)(q_first ? q_heads : kv_heads);
+  p.rope = (uint32_t)rope_dim;
+  p.eps = eps;
+  p.fp8_max = fp8_max;
+  return hip_status(launch_rows(p, (int)head_dim, dtype == RNQ_BF16, true, (hipStream_t)stream), "rnq_qk_norm_rope_fp8");
+}
+
+rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,
+                            void* y, int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
+                            float eps, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
+  if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
+  if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
+  if (M % rows_per_token != 0) return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
+  if (!row_width_ok(N)) return fail(RNQ_ERR_UNSUPPORTED, "N must be 64, 128, 256 or 512 (got %lld)", (long long)N);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if (M == 0) return ok();
+  if (!x || !w || !y) return fail(RNQ_ERR_NULL, "x, w and y are required");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
+  const void* a16[] = {x, w, y, cos, sin};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+
+  RowParams p = {};
+  p.x0 = (const uint16_t*)x;
+  p.w0 = (const uint16_t*)w;
+  p.y0 = (uint16_t*)y;
+  p.cos = cos;
+  p.sin = sin;
+  p.total_rows = (uint32_t)M;
+  p.heads = (uint32_t)rows_per_token;
+  p.heads0 = (uint32_t)rows_per_token;
+  p.rope = (uint32_t)rope_dim;
+  p.eps = eps;
+  p.fp8_max = 448.0f;
+  return hip_status(launch_rows(p, (int)N, dtype == RNQ_BF16, false, (hipStream_t)stream), "rnq_rmsnorm_rope");
+}
+
+rnq_status rnq_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out,
+                           int64_t M, int64_t N, float eps, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
+  if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !y) return fail(RNQ_ERR_NULL, "x, w and y are required");
+  const void* a16[] = {x, w, y};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(rstd_out, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd_out must be 4-byte aligned");
+
+  if (row_width_ok(N)) {
+    RowParams p = {};
+    p.x0 = (const uint16_t*)x;
+    p.w0 = (const uint16_t*)w;
+    p.y0 = (uint16_t*)y;
+    p.rstd = rstd_out;
+    p.total_rows = (uint32_t)M;
+    p.heads = 1;
+    p.heads0 = 1;
+    p.rope = 0;
+    p.eps = eps;
+    p.fp8_max = 448.0f;
+    return hip_status(launch_rows(p, (int)N, dtype == RNQ_BF16, false, (hipStream_t)stream), "rnq_rmsnorm_fwd");
+  }
+  WideFwdParams p = {};
+  p.x = (const uint16_t*)x;
+  p.w = (const uint16_t*)w;
+  p.y = (uint16_t*)y;
+  p.rstd = rstd_out;
+  p.M = (uint32_t)M;
+  p.N = (uint32_t)N;
+  p.eps = eps;
+  return hip_status(launch_wide_fwd(p, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_fwd");
+}
+
+size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
+  if (M <= 0 || N <= 0) return 0;
+  return (size_t)bwd_blocks(M, N) * (size_t)N * sizeof(float);
+}
+
+rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, const float* rstd,
+                           void* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
+                           int64_t M, int64_t N, float eps, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
+  if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !grad_y || !grad_x || !grad_w) return fail(RNQ_ERR_NULL, "x, w, grad_y, grad_x and grad_w are required");
+  const size_t need = rnq_rmsnorm_bwd_workspace_size(M, N);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RNQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes, workspace);
+  const void* a16[] = {x, w, grad_y, grad_x, grad_w, workspace};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
+
+  WideBwdParams p = {};
+  p.x = (const uint16_t*)x;
+  p.w = (const uint16_t*)w;
+  p.gy = (const uint16_t*)grad_y;
+  p.rstd = rstd;
+  p.gx = (uint16_t*)grad_x;
+  p.gw = grad_w;
+  p.partial = (float*)workspace;
+  p.M = (uint32_t)M;
+  p.N = (uint32_t)N;
+  p.blocks = bwd_blocks(M, N);
+  p.rows_per_block = (uint32_t)((M + p.blocks - 1) / p.blocks);
+  p.eps = eps;
+  return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_bwd");
+}
+
+}  // extern "C"

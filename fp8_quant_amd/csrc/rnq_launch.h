@@ -1,0 +1,76 @@
+// Kernel parameter blocks and launchers (internal to librnq.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rnq {
+
+// Rows are (token, head) pairs in token-major order: heads [0, heads0) come
+// from tensor 0 (q or x), heads [heads0, heads) from tensor 1 (k).
+struct RowParams {
+  const uint16_t* x0;
+  const uint16_t* x1;
+  const uint16_t* w0;
+  const uint16_t* w1;
+  const float* cos;  // [tokens, rope/2]
+  const float* sin;
+  uint8_t* c0;  // codes (quantising kernels)
+  uint8_t* c1;
+  float* s0;    // scales
+  float* s1;
+  uint16_t* y0;  // optional y (both or neither)
+  uint16_t* y1;
+  float* rstd;   // optional per-row rstd, flattened row order
+  uint32_t total_rows;
+  uint32_t heads;
+  uint32_t heads0;
+  uint32_t rope;
+  float eps;
+  float fp8_max;
+  // filled by the launcher
+  uint32_t passes;
+  uint32_t passes_per_wave;
+  uint32_t div_magic;
+  uint32_t div_shift;
+};
+
+hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStream_t stream);
+
+struct WideFwdParams {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+  float* rstd;
+  uint32_t M;
+  uint32_t N;
+  float eps;
+};
+
+hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream);
+
+struct WideBwdParams {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* gy;
+  const float* rstd;  // optional
+  uint16_t* gx;
+  float* gw;
+  float* partial;     // [blocks, N] fp32 workspace
+  uint32_t M;
+  uint32_t N;
+  uint32_t rows_per_block;
+  uint32_t blocks;
+  float eps;
+};
+
+// Deterministic row partition used by the backward (and its workspace size).
+uint32_t bwd_blocks(int64_t M, int64_t N);
+hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream);
+
+// Launch-shape knobs (environment, read once): RNQ_TARGET_WAVES, RNQ_PASSES_PER_WAVE.
+uint32_t tuning_target_waves();
+uint32_t tuning_passes_per_wave();
+
+}  // namespace rnq

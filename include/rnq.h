@@ -1,0 +1,149 @@
+/*
+ * rnq - RMSNorm -> partial NeoX RoPE -> per-row FP8 e4m3fn on AMD MI355X (gfx950).
+ *
+ * C ABI of librnq.so. Plain pointers and sizes only; no HIP or torch types.
+ *
+ * Sources of the operations (tilelang-tutorial pages):
+ *  - chapter 13 fusion page "rmsnorm_rope_quant.py": torch_reference_fused and
+ *    the two fused kernels (RMSNorm + RoPE on the last rope_dim columns, then
+ *    per-row absmax FP8 quantisation);
+ *  - chapter 17 page "rmsnorm_tl.py": the RMSNorm forward kernel and
+ *    RMSNormTileLang.backward;
+ *  - chapter 28 page "case_norm_rope_quant.py": the QK-norm prologue (rows are
+ *    (token, head) pairs, one cos/sin row per token shared by every head, one
+ *    fp32 scale per row).
+ *
+ * Common rules for every entry point
+ *  - Memory: every tensor pointer is a device pointer owned by the caller; the
+ *    library never allocates, frees or synchronises. Work is enqueued on
+ *    `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *    runs asynchronously; outputs are fully overwritten. Inputs and outputs
+ *    must not alias.
+ *  - Layout: contiguous row-major. 16-bit float tensors are raw bf16 or fp16
+ *    storage, chosen by `dtype` (rnq_dtype). cos/sin are fp32. FP8 outputs are
+ *    raw e4m3fn bytes (OCP: bias 7, max 448).
+ *  - Alignment: x/q/k/y/grad tensors, weights and cos/sin must be 16-byte
+ *    aligned; FP8 outputs 8-byte aligned; fp32 vectors 4-byte aligned.
+ *  - Arithmetic: fp32 with IEEE rounding at every step and no fused
+ *    multiply-add; the sum of squares of a row is the exact sum rounded once to
+ *    fp32; rsqrt is 1/sqrt with both steps correctly rounded; the normalised
+ *    row and the rotated row are each rounded to the input dtype (nearest
+ *    even); codes are round-to-nearest-even e4m3fn of clamp(y/scale, +-fp8_max).
+ *  - Errors: every argument is validated before anything is enqueued; on a
+ *    non-OK status nothing has been launched (except RNQ_ERR_HIP, reported
+ *    from hipGetLastError after a launch). rnq_status_string() names a status;
+ *    rnq_last_error() gives a per-thread message for the last failed call.
+ *    A call with zero rows returns RNQ_OK and launches nothing.
+ *  - Thread safety: no global mutable state apart from the per-thread error
+ *    message; concurrent calls on different streams are independent.
+ */
+#ifndef RNQ_H_
+#define RNQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rnq_status {
+  RNQ_OK = 0,
+  RNQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  RNQ_ERR_SHAPE = 2,       /* negative size, odd or too large rope_dim, rows not divisible, ... */
+  RNQ_ERR_UNSUPPORTED = 3, /* a width or alignment outside what the kernels are built for */
+  RNQ_ERR_ARG = 4,         /* eps < 0 or non-finite, fp8_max outside (0, 448], unknown dtype */
+  RNQ_ERR_WORKSPACE = 5,   /* workspace too small */
+  RNQ_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} rnq_status;
+
+typedef enum rnq_dtype { RNQ_BF16 = 0, RNQ_F16 = 1 } rnq_dtype;
+
+/* Name of a status code (static string). */
+const char* rnq_status_string(int status);
+
+/* Message describing the last non-OK status returned on the calling thread ("" if none). */
+const char* rnq_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int rnq_abi_version(void);
+
+/*
+ * RMSNorm forward (chapter 17 page, forward kernel; chapter 13 fusion page,
+ * first half of torch_reference_fused):
+ *   rstd[m] = 1 / sqrt(sum_j x[m,j]^2 / N + eps)
+ *   y[m,j]  = round_dtype((x[m,j] * rstd[m]) * w[j])
+ *
+ * x [M,N], w [N], y [M,N] in `dtype`; rstd_out [M] fp32 may be NULL.
+ * N must be a multiple of 8 and at most 16384.
+ */
+rnq_status rnq_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out,
+                           int64_t M, int64_t N, float eps, int dtype, void* stream);
+
+/* Bytes of device workspace rnq_rmsnorm_bwd needs for an [M,N] problem. */
+size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
+
+/*
+ * RMSNorm backward (chapter 17 page, RMSNormTileLang.backward):
+ *   xn = x * rstd, g = grad_y * w, C = sum_j(g * xn) / N
+ *   grad_x = round_dtype(rstd * (g - xn * C))          [M,N] in `dtype`
+ *   grad_w = sum over rows of grad_y * xn              [N] fp32 (the page casts it to
+ *                                                      w's dtype afterwards; the caller may)
+ * rstd [M] fp32 may be NULL, in which case it is recomputed from x as in the
+ * forward. grad_w is reduced deterministically: per-block partial sums over a
+ * fixed row partition are written to `workspace`, then summed in ascending
+ * block order; results are bitwise reproducible for a given (M, N).
+ * workspace_bytes must be >= rnq_rmsnorm_bwd_workspace_size(M, N); the
+ * workspace is scratch owned by the caller (16-byte aligned).
+ */
+rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, const float* rstd,
+                           void* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
+                           int64_t M, int64_t N, float eps, int dtype, void* stream);
+
+/*
+ * RMSNorm + partial NeoX RoPE (chapter 13 fusion page, rms_norm_rope_fused and
+ * _torch_rope_neox):
+ *   n = RMSNorm(x, w) rounded to dtype (as rnq_rmsnorm_fwd)
+ *   on the last R = rope_dim columns, for p < R/2, with c = cos[t,p], s = sin[t,p]:
+ *     y[N-R+p]     = round_dtype(n[N-R+p] * c - n[N-R+R/2+p] * s)
+ *     y[N-R+R/2+p] = round_dtype(n[N-R+R/2+p] * c + n[N-R+p] * s)
+ *   other columns: y = n.
+ * x, y [M,N]; w [N]; cos, sin [M/rows_per_token, R/2] fp32; row m uses table
+ * row t = m / rows_per_token (rows_per_token = heads per token for a
+ * [tokens*heads, head_dim] layout; 1 for one table row per row).
+ * Requirements: N in {64, 128, 256, 512}; R a multiple of 16 with R <= N;
+ * M % rows_per_token == 0. cos/sin may be NULL when R == 0.
+ */
+rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,
+                            void* y, int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
+                            float eps, int dtype, void* stream);
+
+/*
+ * QK-norm + partial NeoX RoPE + per-row FP8 (chapter 28 page, the prologue;
+ * chapter 13 fusion page, rms_norm_rope_quant_fused with one group per row):
+ *   for every (token t, head h) row of q [T,Hq,D] (weight wq) and of
+ *   k [T,Hk,D] (weight wk):
+ *     y     = RMSNorm + RoPE as rnq_rmsnorm_rope, with table row t for every head
+ *     amax  = max_j |y_j|
+ *     scale = max(amax, 1e-4) / fp8_max                      (fp32, one per row)
+ *     code  = e4m3fn(clamp(y_j / scale, -fp8_max, fp8_max))  (nearest even)
+ * Outputs: q_fp8 [T,Hq,D], k_fp8 [T,Hk,D] bytes; q_scale [T,Hq], k_scale [T,Hk]
+ * fp32; q_y / k_y [same as q / k] in dtype, optional (NULL = not written).
+ * k, wk, k_fp8, k_scale may be NULL iff kv_heads == 0.
+ * cos, sin: [T, R/2] fp32 (may be NULL iff rope_dim == 0).
+ * Requirements: D = head_dim in {64, 128, 256, 512}; R = rope_dim a multiple of
+ * 16 with R <= D; 0 < fp8_max <= 448; T*(Hq+Hk) < 2^31.
+ */
+rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, const void* wk,
+                                const float* cos, const float* sin,
+                                uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                void* q_y, void* k_y,
+                                int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, int64_t rope_dim,
+                                float eps, float fp8_max, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNQ_H_ */

@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: the library loads, exports what include/rnq.h declares,
+and rejects bad arguments before launching anything."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_quant_amd as rnq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(rnq.library_path()):
+        pytest.skip("librnq.so not built (run `python -m fp8_quant_amd.build`)")
+    return rnq.load_library()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "rnq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rnq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for must in ("rnq_rmsnorm_fwd", "rnq_rmsnorm_bwd", "rnq_rmsnorm_rope", "rnq_qk_norm_rope_fp8"):
+        assert must in names
+    assert set(names) == set(rnq.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.rnq_abi_version() == 100
+    for s, key in enumerate(["RNQ_OK", "NULL", "SHAPE", "UNSUPPORTED", "ARG", "WORKSPACE", "HIP"]):
+        assert key in lib.rnq_status_string(s).decode()
+    assert b"UNKNOWN" in lib.rnq_status_string(99)
+
+
+def _qk(lib, **kw):
+    a = dict(q=None, k=None, wq=None, wk=None, cos=None, sin=None, q8=None, k8=None, qs=None, ks=None,
+             qy=None, ky=None, T=4, Hq=2, Hk=1, D=128, R=128, eps=1e-6, fp8_max=448.0, dt=0)
+    a.update(kw)
+    return lib.rnq_qk_norm_rope_fp8(a["q"], a["k"], a["wq"], a["wk"], a["cos"], a["sin"], a["q8"], a["k8"],
+                                    a["qs"], a["ks"], a["qy"], a["ky"], a["T"], a["Hq"], a["Hk"], a["D"],
+                                    a["R"], a["eps"], a["fp8_max"], a["dt"], None)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails before any launch
+
+
+def test_qk_argument_validation():
+    lib = _lib()
+    assert _qk(lib) == 1  # NULL pointers
+    assert _qk(lib, T=0) == 0  # no rows: OK, nothing launched
+    assert _qk(lib, T=-1) == 2
+    assert _qk(lib, R=63) == 2  # odd rope_dim
+    assert _qk(lib, R=256) == 2  # rope wider than the row
+    assert _qk(lib, R=40) == 3  # even but not whole chunks
+    assert _qk(lib, D=96, R=32) == 3  # width not built
+    assert _qk(lib, fp8_max=500.0) == 4
+    assert _qk(lib, fp8_max=0.0) == 4
+    assert _qk(lib, eps=-1.0) == 4
+    assert _qk(lib, eps=float("nan")) == 4
+    assert _qk(lib, dt=7) == 4
+    assert _qk(lib, T=1 << 30, Hq=4, Hk=4) == 3  # rows beyond 2^31
+    full = dict(q=FAKE, k=FAKE, wq=FAKE, wk=FAKE, cos=FAKE, sin=FAKE, q8=FAKE, k8=FAKE, qs=FAKE, ks=FAKE)
+    assert _qk(lib, **{**full, "k": None}) == 1  # kv heads need k
+    assert _qk(lib, **{**full, "cos": None}) == 1  # rope needs the table
+    assert _qk(lib, **{**full, "q": ctypes.c_void_p(0x10008)}) == 3  # misaligned
+    assert _qk(lib, **{**full, "qs": ctypes.c_void_p(0x10002)}) == 3
+    assert b"aligned" in lib.rnq_last_error()
+
+
+def test_rmsnorm_argument_validation():
+    lib = _lib()
+    assert lib.rnq_rmsnorm_fwd(None, None, None, None, 4, 4096, 1e-6, 0, None) == 1
+    assert lib.rnq_rmsnorm_fwd(None, None, None, None, 0, 4096, 1e-6, 0, None) == 0
+    assert lib.rnq_rmsnorm_fwd(FAKE, FAKE, FAKE, None, 4, 4100, 1e-6, 0, None) == 3
+    assert lib.rnq_rmsnorm_fwd(FAKE, FAKE, FAKE, None, 4, 32768, 1e-6, 0, None) == 3
+    assert lib.rnq_rmsnorm_fwd(FAKE, FAKE, FAKE, None, -4, 4096, 1e-6, 0, None) == 2
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 128, 64, 4, 1e-6, 0, None) == 2
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 128, 64, 1, 1e-6, 0, None) == 1
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 3
+    need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 4096)
+    assert need == 256 * 4096 * 4
+    assert lib.rnq_rmsnorm_bwd_workspace_size(0, 4096) == 0
+    assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, 4096, 4096, 1e-6, 0, None) == 5
+    assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, need, 4096, 4096, 1e-6, 0, None) == 5
+    assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, None, None, FAKE, FAKE, FAKE, need, 4096, 4096, 1e-6, 0, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    _lib()
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        rnq.rmsnorm(x, torch.zeros(128, dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(rnq, "_lib", None)
+    monkeypatch.setenv("RNQ_LIBRARY", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        rnq.load_library()

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bar: bit-exact y, codes and scales on every row whose sum of squares the
+oracle proves exact in fp64 (all rows of these workloads in practice); on any
+other row |dy| <= 1 ulp, codes within one step on <= 0.01 % of elements and
+scale relative error <= 1e-6. Backward: |a - b| <= 2e-2 * (|b| + rms of the
+reference row / column).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_quant_amd as rnq
+import oracle
+import workloads
+from oracle import codecs
+
+from _parity import (
+    assert_rows_match,
+    compare_qk,
+    gpu,
+    oracle_qk,
+    run_qk_gpu,
+    unproven_rows,
+    ulp_distance_16,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+def _qk_case(T, Hq, Hk, D, R, seed, dtype=torch.bfloat16, std=1.0, outliers=0.0, theta=10000.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(T, Hq, D, generator=g) * std
+    k = torch.randn(T, Hk, D, generator=g) * std
+    if outliers:
+        q = torch.where(torch.rand(q.shape, generator=g) < outliers, q * 20, q)
+        k = torch.where(torch.rand(k.shape, generator=g) < outliers, k * 20, k)
+    wq = 1 + 0.1 * torch.randn(D, generator=g)
+    wk = 1 + 0.1 * torch.randn(D, generator=g)
+    cos, sin = workloads.rope_table(np.arange(T), R, theta)
+    return {"q": q.to(dtype), "k": k.to(dtype), "wq": wq.to(dtype), "wk": wk.to(dtype),
+            "cos": torch.from_numpy(cos), "sin": torch.from_numpy(sin)}
+
+
+def _check_qk(name, d, *, eps=1e-6, fp8_max=448.0, with_y=True):
+    dt = "bf16" if d["q"].dtype == torch.bfloat16 else "fp16"
+    print(f"[parity] {name}: q{tuple(d['q'].shape)} k{tuple(d['k'].shape)} rope {2 * d['cos'].shape[-1]}", flush=True)
+    got = run_qk_gpu(d, eps=eps, fp8_max=fp8_max, with_y=with_y)
+    ref = oracle_qk(d, eps=eps, fp8_max=fp8_max)
+    compare_qk(name, d, got, ref, dt)
+    return got, ref
+
+
+# ------------------------------------------------------------------ named workloads
+
+
+def test_qk_small_fused_partial_rope_with_y():
+    d = workloads.generate("qk_small")
+    got, ref = _check_qk("qk_small", d, with_y=True)
+    assert got["q_y"] is not None
+
+
+def test_qk_4k_full_size():
+    """4096 tokens x (32 + 8) heads x 128, every row, in the launch shape the bench times (no y)."""
+    d = workloads.generate("qk_4k")
+    got, ref = _check_qk("qk_4k", d, with_y=False)
+    # and again with y written, which exposes the rounded rows themselves
+    got_y = run_qk_gpu(d, with_y=True)
+    compare_qk("qk_4k+y", d, got_y, ref)
+    assert np.array_equal(got_y["q_codes"], got["q_codes"])
+
+
+def test_qk_64k_sampled_rows():
+    """65536 tokens x (64 + 8) heads x 128: every head of the first and last token and
+    65536 seeded random rows, each checked against the oracle."""
+    d = workloads.generate("qk_64k")
+    print("[parity] qk_64k generated", flush=True)
+    got = run_qk_gpu(d, with_y=False)
+    T, Hq, D = d["q"].shape
+    Hk = d["k"].shape[1]
+    rng = np.random.default_rng(2024)
+    for part, H in (("q", Hq), ("k", Hk)):
+        rows = np.unique(np.concatenate([
+            np.arange(H), (T - 1) * H + np.arange(H), rng.integers(0, T * H, 32768)]))
+        toks, heads = rows // H, rows % H
+        xb = workloads.bits(d[part]).reshape(T * H, D)[rows]
+        wb = workloads.bits(d["w" + part])
+        c, s = d["cos"].numpy()[toks], d["sin"].numpy()[toks]
+        y, codes, scale = oracle.norm_rope_quant_rows(xb, wb, c, s, 1e-6, 448.0)
+        gc = got[part + "_codes"].reshape(T * H, D)[rows]
+        gs = got[part + "_scale"].reshape(T * H)[rows]
+        assert_rows_match(f"qk_64k/{part}", None, gc, gs, None, codes, scale, unproven_rows(xb, "bf16"))
+
+
+def test_norm_rope_fp16_full_size():
+    d = workloads.generate("norm_rope_fp16")
+    x, w = gpu(d["x"]), gpu(d["w"])
+    y = rnq.rmsnorm_rope(x, w, gpu(d["cos"]), gpu(d["sin"]), rows_per_token=1)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_rope(workloads.bits(d["x"]), workloads.bits(d["w"]), d["cos"].numpy(),
+                              d["sin"].numpy(), dtype="fp16")
+    xb = workloads.bits(d["x"])
+    assert_rows_match("norm_rope_fp16", workloads.bits(y), None, None, ref, None, None, unproven_rows(xb, "fp16"))
+
+
+def test_rmsnorm_4k_forward_and_rstd():
+    d = workloads.generate("rmsnorm_4k")
+    x, w = gpu(d["x"]), gpu(d["w"])
+    y, rstd = rnq.rmsnorm(x, w, return_rstd=True)
+    torch.cuda.synchronize()
+    ref_y, ref_rstd = oracle.rmsnorm_fwd(workloads.bits(d["x"]), workloads.bits(d["w"]), 1e-6)
+    loose = unproven_rows(workloads.bits(d["x"]), "bf16")
+    assert_rows_match("rmsnorm_4k", workloads.bits(y), None, None, ref_y, None, None, loose)
+    r = rstd.cpu().numpy()
+    assert np.array_equal(r.view(np.uint32)[~loose], ref_rstd.view(np.uint32)[~loose])
+
+
+def _bwd_check(name, x, w, gy, gx, gw, rstd_given=None):
+    ref_dx, ref_dw, _ = oracle.rmsnorm_bwd(workloads.bits(x), workloads.bits(w), workloads.bits(gy), 1e-6,
+                                           "bf16" if x.dtype == torch.bfloat16 else "fp16", rstd=rstd_given)
+    dt = "bf16" if x.dtype == torch.bfloat16 else "fp16"
+    dx = codecs.dtype_to_f32(workloads.bits(gx), dt).astype(np.float64)
+    dw = gw.cpu().numpy().astype(np.float64)
+    row_rms = np.sqrt((ref_dx**2).mean(axis=1, keepdims=True))
+    err = np.abs(dx - ref_dx) / (np.abs(ref_dx) + row_rms)
+    assert err.max() <= 2e-2, f"{name}: dx rel err {err.max():.3g}"
+    col_rms = np.sqrt((ref_dw**2).mean())
+    errw = np.abs(dw - ref_dw) / (np.abs(ref_dw) + col_rms)
+    assert errw.max() <= 2e-2, f"{name}: dw rel err {errw.max():.3g}"
+    print(f"[parity] {name}: max rel err dx {err.max():.3g} dw {errw.max():.3g}", flush=True)
+
+
+def test_rmsnorm_4k_backward_and_determinism():
+    d = workloads.generate("rmsnorm_4k")
+    x, w, gy = gpu(d["x"]), gpu(d["w"]), gpu(d["grad_y"])
+    gx, gw = rnq.rmsnorm_bwd(x, w, gy)
+    gx2, gw2 = rnq.rmsnorm_bwd(x, w, gy)
+    torch.cuda.synchronize()
+    _bwd_check("rmsnorm_4k bwd", d["x"], d["w"], d["grad_y"], gx, gw)
+    assert torch.equal(gx, gx2) and torch.equal(gw.view(torch.int32), gw2.view(torch.int32))
+    # with the rstd saved by the forward
+    _, rstd = rnq.rmsnorm(x, w, return_rstd=True)
+    gx3, gw3 = rnq.rmsnorm_bwd(x, w, gy, rstd)
+    torch.cuda.synchronize()
+    assert torch.equal(gx3, gx) and torch.equal(gw3.view(torch.int32), gw.view(torch.int32))
+
+
+# ------------------------------------------------------------------ shapes and edges
+
+
+@pytest.mark.parametrize(
+    "T,Hq,Hk,D,R",
+    [
+        (37, 3, 2, 128, 64),   # rows not a multiple of a pass; passes mix q and k rows
+        (5, 1, 0, 128, 128),   # a single partial pass
+        (1, 1, 1, 128, 128),
+        (64, 4, 4, 64, 16),
+        (33, 2, 1, 256, 128),
+        (17, 2, 2, 512, 256),
+        (50, 8, 8, 128, 0),    # no rope: plain RMSNorm + FP8
+        (40, 0, 3, 128, 64),   # k heads only
+        (300, 32, 8, 128, 128),
+    ],
+)
+def test_qk_shapes(T, Hq, Hk, D, R):
+    d = _qk_case(T, Hq, Hk, D, R, seed=T * 1000 + Hq * 10 + Hk + D + R)
+    _check_qk(f"qk T{T} Hq{Hq} Hk{Hk} D{D} R{R}", d)
+
+
+def test_qk_fp16_inputs_and_smaller_fp8_max():
+    d = _qk_case(64, 4, 2, 128, 64, seed=77, dtype=torch.float16, std=3.0)
+    _check_qk("qk fp16", d, fp8_max=448.0)
+    d = _qk_case(64, 4, 2, 128, 128, seed=78, outliers=0.05)
+    _check_qk("qk fp8_max 240", d, fp8_max=240.0)
+    _check_qk("qk fp8_max 57.5", d, fp8_max=57.5)
+
+
+def test_qk_degenerate_rows():
+    """Zero rows (codes keep the sign of w), constant rows, tiny and huge values, eps = 0."""
+    d = _qk_case(16, 4, 2, 128, 64, seed=79)
+    q = d["q"].float()
+    q[0] = 0.0
+    q[1] = 1.0
+    q[2] = -3.0
+    q[3, :, :64] = 0.0
+    q[4] *= 1e-30
+    q[5] *= 1e30
+    q[6, 0, 5] = 1e4
+    d["q"] = q.to(torch.bfloat16)
+    wq = d["wq"].float()
+    wq[::3] *= -1
+    d["wq"] = wq.to(torch.bfloat16)
+    _check_qk("qk degenerate", d)
+    # eps = 0 on rows whose sum of squares stays a normal fp32 number
+    d2 = _qk_case(16, 4, 2, 128, 64, seed=84)
+    q2 = d2["q"].float()
+    q2[0] = 0.25
+    q2[1, :, 7] = -2.0
+    d2["q"] = q2.to(torch.bfloat16)
+    _check_qk("qk eps 0", d2, eps=0.0)
+
+
+def test_qk_zero_tokens_is_a_no_op():
+    d = _qk_case(0, 4, 2, 128, 64, seed=80)
+    got = run_qk_gpu(d)
+    assert got["q_codes"].size == 0
+
+
+def test_qk_repeatable_bitwise():
+    d = _qk_case(256, 32, 8, 128, 128, seed=81, outliers=0.01)
+    a = run_qk_gpu(d)
+    b = run_qk_gpu(d)
+    for key in ("q_codes", "k_codes"):
+        assert np.array_equal(a[key], b[key])
+    for key in ("q_scale", "k_scale"):
+        assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [64, 128, 256, 512, 72, 1000, 2048, 4104, 16384])
+def test_rmsnorm_widths(N):
+    M = 33
+    g = torch.Generator("cpu").manual_seed(N)
+    x = (torch.randn(M, N, generator=g) * 2).to(torch.bfloat16)
+    w = torch.randn(N, generator=g).to(torch.bfloat16)
+    x[3] = 0
+    print(f"[parity] rmsnorm M{M} N{N}", flush=True)
+    y, rstd = rnq.rmsnorm(gpu(x), gpu(w), return_rstd=True)
+    torch.cuda.synchronize()
+    ref_y, ref_rstd = oracle.rmsnorm_fwd(workloads.bits(x), workloads.bits(w), 1e-6)
+    loose = unproven_rows(workloads.bits(x), "bf16")
+    assert_rows_match(f"rmsnorm N{N}", workloads.bits(y), None, None, ref_y, None, None, loose)
+    assert np.array_equal(rstd.cpu().numpy().view(np.uint32)[~loose], ref_rstd.view(np.uint32)[~loose])
+
+
+@pytest.mark.parametrize("M,N", [(1, 128), (3, 4104), (257, 1024), (1000, 512), (64, 16384)])
+def test_rmsnorm_bwd_shapes(M, N):
+    g = torch.Generator("cpu").manual_seed(M * 7 + N)
+    x = torch.randn(M, N, generator=g).to(torch.bfloat16)
+    w = torch.randn(N, generator=g).to(torch.bfloat16)
+    gy = torch.randn(M, N, generator=g).to(torch.bfloat16)
+    gx, gw = rnq.rmsnorm_bwd(gpu(x), gpu(w), gpu(gy))
+    torch.cuda.synchronize()
+    _bwd_check(f"bwd M{M} N{N}", x, w, gy, gx, gw)
+
+
+def test_rmsnorm_rope_grouped_table_rows():
+    """rows_per_token > 1: every head of a token reads that token's table row."""
+    T, H, N, R = 50, 6, 128, 64
+    g = torch.Generator("cpu").manual_seed(82)
+    x = torch.randn(T * H, N, generator=g).to(torch.bfloat16)
+    w = (1 + 0.1 * torch.randn(N, generator=g)).to(torch.bfloat16)
+    cos, sin = workloads.rope_table(np.arange(T) * 3, R, 10000.0)
+    y = rnq.rmsnorm_rope(gpu(x), gpu(w), gpu(torch.from_numpy(cos)), gpu(torch.from_numpy(sin)), rows_per_token=H)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_rope(workloads.bits(x), workloads.bits(w), cos, sin, rows_per_token=H)
+    assert_rows_match("rmsnorm_rope grouped", workloads.bits(y), None, None, ref, None, None,
+                      unproven_rows(workloads.bits(x), "bf16"))
+
+
+def test_cross_entry_rope_zero_equals_rmsnorm():
+    g = torch.Generator("cpu").manual_seed(83)
+    x = torch.randn(100, 256, generator=g).to(torch.bfloat16)
+    w = torch.randn(256, generator=g).to(torch.bfloat16)
+    a = rnq.rmsnorm(gpu(x), gpu(w))
+    b = rnq.rmsnorm_rope(gpu(x), gpu(w), None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_invalid_arguments_raise_before_launch():
+    x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rnq.RnqError) as e:
+        rnq.rnq_rmsnorm_rope(x, w, None, None, torch.empty_like(x), rows_per_token=3)
+    assert e.value.status == 2
+    with pytest.raises(rnq.RnqError) as e:
+        rnq.qk_norm_rope_fp8(x.view(4, 1, 128), None, w, None,
+                             torch.zeros(4, 64, device="cuda"), torch.zeros(4, 64, device="cuda"), fp8_max=500.0)
+    assert e.value.status == 4
+    with pytest.raises(ValueError):
+        rnq.rmsnorm(x.cpu(), w.cpu())  # no CPU path
