@@ -60,6 +60,21 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return v;
 }
 
+// ------------------------------------------------------- streaming accesses
+// Data read once and codes written once: nontemporal hint (no reuse in cache).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream8(void* p, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, (u32x2*)p);
+}
+
 // ------------------------------------------------------------ DPP reductions
 // dpp_ctrl values (GFX9 DPP): quad_perm [1,0,3,2] = 0xB1 (xor 1),
 // quad_perm [2,3,0,1] = 0x4E (xor 2), row_half_mirror = 0x141 (lane i <- 7-i
@@ -67,14 +82,14 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   uint64_t b = __builtin_bit_cast(uint64_t, v);
-  int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
@@ -102,37 +117,78 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Max over aligned groups of L lanes of non-negative finite values
+// (IEEE-2019 maximum: no input canonicalisation needed).
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
-  if constexpr (L >= 2) v = fmaxf(v, dpp_f32<0xB1>(v));
-  if constexpr (L >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));
-  if constexpr (L >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
-  if constexpr (L >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
-  if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
-  if constexpr (L >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  if constexpr (L >= 2) v = __builtin_elementwise_maximum(v, dpp_f32<0xB1>(v));
+  if constexpr (L >= 4) v = __builtin_elementwise_maximum(v, dpp_f32<0x4E>(v));
+  if constexpr (L >= 8) v = __builtin_elementwise_maximum(v, dpp_f32<0x141>(v));
+  if constexpr (L >= 16) v = __builtin_elementwise_maximum(v, dpp_f32<0x140>(v));
+  if constexpr (L >= 32) v = __builtin_elementwise_maximum(v, __shfl_xor(v, 16, 64));
+  if constexpr (L >= 64) v = __builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64));
   return v;
 }
 
 // ------------------------------------------------------------- row scalars
+// The row scalars are correctly rounded IEEE results. Each has a short
+// sequence, checked bit for bit against the IEEE one over every input in its
+// range (all normal positive floats for the reciprocal; v >= 2^-105 for the
+// square root), and the IEEE sequence (which hipcc emits for '/' and
+// __builtin_sqrtf) for anything outside that range.
 
-// 1 / sqrt(v): correctly rounded square root, then correctly rounded division
-// (hipcc lowers __builtin_sqrtf and '/' to IEEE-exact sequences).
-__device__ __forceinline__ float rstd_of(float v) { return 1.0f / __builtin_sqrtf(v); }
+// RN(1/s) for s in [2^-126, 2^126): hardware reciprocal (1 ulp) and one
+// Newton step, r = r0 + r0 (1 - s r0) with fused multiply-adds.
+__device__ __forceinline__ float rcp_rn_fast(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
 
-// y / scale rounded to nearest, from r = RN(1/scale): q0 = RN(y r), the exact
-// residual e = scale*q0 - y by one FMA, then q1 = RN(q0 - e r). For every
-// bf16 or fp16 y and every fp32 scale this equals the IEEE quotient whenever
-// |y/scale| >= 2^-100; below that both are far under the smallest e4m3
-// subnormal and carry the same sign. Zeros keep their sign.
-__device__ __forceinline__ float div_by_scale(float y, float scale, float r) {
-  float q0 = y * r;
-  float e = __builtin_fmaf(scale, q0, -y);
+// RN(sqrt(v)) for v in [2^-105, +inf]: hardware square root (1 ulp), then
+// the neighbour whose square brackets v.
+__device__ __forceinline__ float sqrt_rn_fast(float v) {
+  float s = __builtin_amdgcn_sqrtf(v);
+  const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rm = __builtin_fmaf(-sm, s, v);
+  const float rp = __builtin_fmaf(-sp, s, v);
+  s = (rm <= 0.0f) ? sm : s;
+  s = (rp > 0.0f) ? sp : s;
+  return s;
+}
+
+// rstd = RN(1 / RN(sqrt(v))), v = mean(x^2) + eps. All lanes of a wave take
+// the same branch (the fast one unless some row is outside the checked range).
+__device__ __forceinline__ float rstd_of(float v) {
+  const bool fast = v >= 0x1p-100f && v <= 0x1p+120f;
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0) return rcp_rn_fast(sqrt_rn_fast(v));
+  return 1.0f / __builtin_sqrtf(v);
+}
+
+// RN(1/s) for any positive normal s (fast path below 2^126).
+__device__ __forceinline__ float rcp_rn(float s) {
+  if (__builtin_amdgcn_ballot_w64(!(s < 0x1p+126f)) == 0) return rcp_rn_fast(s);
+  return 1.0f / s;
+}
+
+// a / b rounded to nearest, given r = RN(1/b): q0 = RN(a r), the exact
+// residual e = b*q0 - a by one FMA, then q1 = RN(q0 - e r). Checked bit for
+// bit against IEEE division for every a with at most 11 significand bits
+// (every bf16 or fp16 value) and every fp32 b, at normal exponents; the result
+// differs only where |a/b| < 2^-100 (and then keeps the sign), which for the
+// FP8 step is far below the smallest e4m3 subnormal. Zeros keep their sign.
+__device__ __forceinline__ float div_by(float a, float b, float r) {
+  const float q0 = a * r;
+  const float e = __builtin_fmaf(b, q0, -a);
   return __builtin_fmaf(-e, r, q0);
 }
 
 // Four values -> four e4m3fn codes (OCP, nearest even) in one 32-bit word.
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// The first conversion fills the low half; the previous contents of the word
+// do not matter, so any register serves as its initial value.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, uint32_t any) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)any, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }

@@ -30,6 +30,9 @@ struct RowParams {
   float eps;
   float fp8_max;
   // filled by the launcher
+  float rcp_fp8_max;   // RN(1 / fp8_max)
+  float scale_floor;   // RN(1e-4 / fp8_max)
+  uint32_t scale_by_rcp;
   uint32_t passes;
   uint32_t passes_per_wave;
   uint32_t div_magic;

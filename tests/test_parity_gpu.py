@@ -176,6 +176,10 @@ def test_qk_fp16_inputs_and_smaller_fp8_max():
     d = _qk_case(64, 4, 2, 128, 128, seed=78, outliers=0.05)
     _check_qk("qk fp8_max 240", d, fp8_max=240.0)
     _check_qk("qk fp8_max 57.5", d, fp8_max=57.5)
+    # 58 lies on an e4m3 rounding boundary (between 56 and 60): the clamp binds
+    _check_qk("qk fp8_max 58 (clamped)", d, fp8_max=58.0)
+    # below 1 the scale takes the IEEE division path
+    _check_qk("qk fp8_max 0.5", d, fp8_max=0.5)
 
 
 def test_qk_degenerate_rows():
@@ -199,6 +203,7 @@ def test_qk_degenerate_rows():
     q2 = d2["q"].float()
     q2[0] = 0.25
     q2[1, :, 7] = -2.0
+    q2[2] *= 1e-20  # mean(x^2) far below 2^-100: the IEEE rstd path
     d2["q"] = q2.to(torch.bfloat16)
     _check_qk("qk eps 0", d2, eps=0.0)
 
