@@ -5,11 +5,13 @@ One step = one ``rnq_qk_norm_rope_fp8`` call over the whole batch (RMSNorm ->
 NeoX RoPE -> per-row FP8 for every (token, head) row). Inputs are seeded
 synthetic tensors already resident in HBM; several input/output sets are
 rotated so the working set (> 512 MB) does not stay in the 256 MB Infinity
-Cache between steps.
+Cache between steps. The K timed steps are launched back to back with
+pre-marshalled arguments between two events on the launch stream, so the
+time per step is the kernel's own time (the host stays ahead of the GPU).
 
 Prints ONE JSON line: achieved GB/s (algorithmic bytes / step time), % of the
-8 TB/s HBM peak, rows/s, the roofline of the kernel (average launch time from
-HIP events on the launch stream), and the CPU oracle timed on a bounded sample.
+8 TB/s HBM peak, rows/s, the roofline of the kernel, the other paths of the
+library measured the same way, and the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -17,6 +19,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -29,6 +32,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.hip", "fp8_quant_amd/csrc/rnq_device.h",
                   "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
+ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
 
 
 def kernel_source_hash() -> str:
@@ -50,6 +54,120 @@ def measured_traffic():
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU timing
+
+
+def _timed(torch, launches, steps, warmup):
+    """Warm up, then time ``steps`` back-to-back launches (rotating over the
+    prepared launchers) between two events on the launch stream; ms per step.
+    Each launcher holds pre-marshalled arguments, so the host enqueues a call in
+    a few microseconds and the GPU runs the kernels back to back."""
+    n = len(launches)
+    for i in range(warmup):
+        launches[i % n]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        launches[i % n]()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def _n_sets(nbytes: int) -> int:
+    return max(1, min(64, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
+
+
+def bench_qk(torch, rnq, workloads, ledger, name, steps, warmup):
+    wl = workloads.WORKLOADS[name]
+    d = workloads.generate(name)
+    T, Hq, Hk, D, R = d["tokens"], d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"]
+    led = ledger.qk_bytes(T, Hq, Hk, D, R, write_y=wl.write_y)
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(led["total"])
+    sets = []
+    for _ in range(n_sets):
+        s = {"q": d["q"].to(dev), "k": d["k"].to(dev) if Hk else None,
+             "q8": torch.empty((T, Hq, D), dtype=torch.uint8, device=dev),
+             "k8": torch.empty((T, Hk, D), dtype=torch.uint8, device=dev) if Hk else None,
+             "qs": torch.empty((T, Hq), dtype=torch.float32, device=dev),
+             "ks": torch.empty((T, Hk), dtype=torch.float32, device=dev) if Hk else None}
+        s["qy"] = torch.empty_like(s["q"]) if wl.write_y else None
+        sets.append(s)
+    wq = d["wq"].to(dev)
+    wk = d["wk"].to(dev) if Hk else None
+    cos, sin = d["cos"].to(dev), d["sin"].to(dev)
+    del d
+
+    launches = [rnq.prepare_qk_norm_rope_fp8(s["q"], s["k"], wq, wk, cos, sin, s["q8"], s["k8"], s["qs"], s["ks"],
+                                             s["qy"], None, eps=wl.eps, fp8_max=wl.fp8_max) for s in sets]
+    ms = _timed(torch, launches, steps, warmup)
+    out = {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_norm_rope(torch, rnq, workloads, ledger, name, steps, warmup):
+    d = workloads.generate(name)
+    M, N, R = d["rows"], d["width"], d["rope_dim"]
+    led = ledger.norm_rope_bytes(M, N, R, d["rows_per_token"])
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(led["total"])
+    sets = [{"x": d["x"].to(dev), "y": torch.empty_like(d["x"], device=dev),
+             "cos": d["cos"].to(dev), "sin": d["sin"].to(dev)} for _ in range(n_sets)]
+    w = d["w"].to(dev)
+
+    launches = [rnq.prepare_rmsnorm_rope(s["x"], w, s["cos"], s["sin"], s["y"], rows_per_token=d["rows_per_token"])
+                for s in sets]
+    ms = _timed(torch, launches, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
+
+
+def bench_rmsnorm(torch, rnq, workloads, ledger, name, steps, warmup):
+    d = workloads.generate(name)
+    M, N = d["rows"], d["width"]
+    fwd = ledger.rmsnorm_fwd_bytes(M, N)
+    bwd = ledger.rmsnorm_bwd_bytes(M, N)
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(bwd["total"])
+    ws_bytes = rnq.rnq_rmsnorm_bwd_workspace_size(M, N)
+    sets = [{"x": d["x"].to(dev), "gy": d["grad_y"].to(dev), "y": torch.empty_like(d["x"], device=dev),
+             "gx": torch.empty_like(d["x"], device=dev),
+             "gw": torch.empty((N,), dtype=torch.float32, device=dev),
+             "ws": torch.empty((max(ws_bytes, 16) // 4,), dtype=torch.float32, device=dev)} for _ in range(n_sets)]
+    w = d["w"].to(dev)
+
+    ms_f = _timed(torch, [rnq.prepare_rmsnorm_fwd(s["x"], w, s["y"]) for s in sets], steps, warmup)
+    ms_b = _timed(torch, [rnq.prepare_rmsnorm_bwd(s["x"], w, s["gy"], s["gx"], s["gw"], s["ws"]) for s in sets],
+                  steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return [
+        {"workload": name + " fwd", "ms": ms_f, "bytes": fwd["total"], "rows": M, "sets": n_sets},
+        {"workload": name + " bwd", "ms": ms_b, "bytes": bwd["total"], "rows": M, "sets": n_sets,
+         "workspace_bytes_each_way": ws_bytes},
+    ]
+
+
+def _summary(r):
+    gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+    out = {"workload": r["workload"], "us_per_call": round(r["ms"] * 1e3, 3), "GB/s": round(gbs, 1),
+           "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "rows_per_s": round(r["rows"] / (r["ms"] * 1e-3), 1),
+           "bytes": r["bytes"], "rotated_sets": r["sets"]}
+    for k in ("workspace_bytes_each_way",):
+        if k in r:
+            out[k] = r[k]
+    return out
+
+
+# ---------------------------------------------------------------- CPU oracle
 
 
 def cpu_baseline(workload_name: str, budget_s: float = 12.0) -> dict:
@@ -80,7 +198,8 @@ def cpu_baseline(workload_name: str, budget_s: float = 12.0) -> dict:
         "rows_per_s": round(b["rows"] / dt, 1),
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {done} of {T} tokens ({b['rows']} rows), numpy oracle, one pass, {dt:.1f} s",
+        "sample": f"first {done} of {T} tokens ({b['rows']} rows) of {workload_name}, numpy oracle "
+                  f"(single thread), one pass, {dt:.1f} s",
     }
 
 
@@ -90,13 +209,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qk_4k")
-    ap.add_argument("--sets", type=int, default=0, help="rotated input/output sets (0 = enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-paths", action="store_true", help="time only the headline workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by token with no exchange, see DESIGN.md", file=sys.stderr)
+              "the rows are independent and the path would shard by token with no exchange", file=sys.stderr)
         return 2
 
     import torch
@@ -105,94 +224,53 @@ def main() -> int:
     import workloads
     from fp8_quant_amd import ledger
 
+    torch.cuda.set_device(0)
+    head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup)
     wl = workloads.WORKLOADS[args.workload]
-    assert wl.kind == "qk", "the bench times the QK-norm + RoPE + FP8 path"
-    d = workloads.generate(args.workload)
-    T, Hq, Hk, D, R = d["tokens"], d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"]
-    led = ledger.qk_bytes(T, Hq, Hk, D, R)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    n_sets = args.sets or max(2, -(-512 * 2**20 // led["total"]) + 1)
-    sets = []
-    for _ in range(n_sets):
-        sets.append({
-            "q": d["q"].to(dev), "k": d["k"].to(dev),
-            "q8": torch.empty((T, Hq, D), dtype=torch.uint8, device=dev),
-            "k8": torch.empty((T, Hk, D), dtype=torch.uint8, device=dev),
-            "qs": torch.empty((T, Hq), dtype=torch.float32, device=dev),
-            "ks": torch.empty((T, Hk), dtype=torch.float32, device=dev),
-        })
-    wq, wk = d["wq"].to(dev), d["wk"].to(dev)
-    cos, sin = d["cos"].to(dev), d["sin"].to(dev)
-    torch.cuda.synchronize()
-
-    def step(i):
-        s = sets[i % n_sets]
-        rnq.rnq_qk_norm_rope_fp8(s["q"], s["k"], wq, wk, cos, sin, s["q8"], s["k8"], s["qs"], s["ks"],
-                                 eps=wl.eps, fp8_max=wl.fp8_max)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record()
-        step(args.warmup + i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
-    region_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = region_ms / K
-    kern_ms = sum(per_launch_ms) / K
-    per_launch_sorted = sorted(per_launch_ms)
-
-    value = led["total"] / (ms_per_step * 1e-3) / 1e9
-    achieved = led["total"] / (kern_ms * 1e-3) / 1e9
+    ms = head["ms"]
+    value = head["bytes"] / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: QK-norm+RoPE+FP8, {T} tokens x ({Hq} q + {Hk} kv) heads x {D}, "
-                        f"rope {R}, bf16 in, e4m3fn + fp32 scale per row out",
-            "tokens": T, "q_heads": Hq, "kv_heads": Hk, "head_dim": D, "rope_dim": R,
-            "rotated_sets": n_sets,
+            "workload": f"{args.workload}: QK-norm+RoPE+FP8, {wl.tokens} tokens x ({wl.q_heads} q + "
+                        f"{wl.kv_heads} kv) heads x {wl.head_dim}, rope {wl.rope_dim}, bf16 in, "
+                        f"e4m3fn + fp32 scale per row out",
+            "tokens": wl.tokens, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
+            "head_dim": wl.head_dim, "rope_dim": wl.rope_dim,
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "rows_per_s": round(led["rows"] / (ms_per_step * 1e-3), 1),
-        "bytes_per_step": led["total"],
-        "kernel_ms": {"mean": round(kern_ms, 6), "p10": round(per_launch_sorted[K // 10], 6),
-                      "p50": round(per_launch_sorted[K // 2], 6), "p90": round(per_launch_sorted[(9 * K) // 10], 6)},
+        "rows_per_s": round(head["rows"] / (ms * 1e-3), 1),
+        "bytes_per_step": head["bytes"],
+        "rotated_sets": head["sets"],
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 2),
+            "achieved": round(value, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "frac": round(value / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(),
         },
-        "host_wall_s": round(wall, 4),
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
-    else:
-        out["cpu_baseline"] = None
+    if not args.no_other_paths:
+        paths = []
+        steps = max(10, args.steps // 4)
+        paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_small", steps, args.warmup)))
+        paths += [_summary(r) for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, args.warmup)]
+        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, args.warmup)))
+        paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 3)))
+        out["other_paths"] = paths
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -28,6 +28,10 @@ __all__ = [
     "rnq_rmsnorm_fwd",
     "rnq_rmsnorm_bwd",
     "rnq_rmsnorm_bwd_workspace_size",
+    "prepare_qk_norm_rope_fp8",
+    "prepare_rmsnorm_rope",
+    "prepare_rmsnorm_fwd",
+    "prepare_rmsnorm_bwd",
     "qk_norm_rope_fp8",
     "rmsnorm",
     "rmsnorm_bwd",
@@ -164,6 +168,22 @@ def rnq_abi_version() -> int:
 def rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None,
                          *, eps: float = 1e-6, fp8_max: float = 448.0, stream=None) -> None:
     """QK-norm + RoPE + FP8 into caller-provided outputs (see include/rnq.h)."""
+    prepare_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y, k_y,
+                             eps=eps, fp8_max=fp8_max, stream=stream)()
+
+
+def _launcher(fn, args):
+    def launch():
+        status = fn(*args)
+        if status != 0:
+            _check(status)
+    return launch
+
+
+def prepare_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None,
+                             *, eps: float = 1e-6, fp8_max: float = 448.0, stream=None):
+    """Check and marshal the arguments once; returns a zero-argument callable that
+    enqueues ``rnq_qk_norm_rope_fp8`` on the stream (for tight launch loops)."""
     torch = _torch()
     lib = load_library()
     T, Hq, D = q.shape
@@ -186,15 +206,19 @@ def rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale,
     _expect(k_scale, torch.float32, (T, Hk), "k_scale")
     _expect(q_y, dt, (T, Hq, D), "q_y")
     _expect(k_y, dt, (T, Hk, D), "k_y")
-    status = lib.rnq_qk_norm_rope_fp8(
+    args = (
         _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(cos), _ptr(sin),
         _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale), _ptr(k_scale), _ptr(q_y), _ptr(k_y),
         T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
     )
-    _check(status)
+    return _launcher(lib.rnq_qk_norm_rope_fp8, args)
 
 
 def rnq_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float = 1e-6, stream=None) -> None:
+    prepare_rmsnorm_rope(x, w, cos, sin, y, rows_per_token=rows_per_token, eps=eps, stream=stream)()
+
+
+def prepare_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float = 1e-6, stream=None):
     torch = _torch()
     lib = load_library()
     M, N = x.shape
@@ -204,20 +228,24 @@ def rnq_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float =
     if cos is not None:
         _expect(cos, torch.float32, (M // max(rows_per_token, 1), half), "cos")
         _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
-    status = lib.rnq_rmsnorm_rope(_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), M, N, 2 * half,
-                                  rows_per_token, eps, _dtype_code(x), _stream(x, stream))
-    _check(status)
+    args = (_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), M, N, 2 * half,
+            rows_per_token, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_rope, args)
 
 
 def rnq_rmsnorm_fwd(x, w, y, rstd=None, *, eps: float = 1e-6, stream=None) -> None:
+    prepare_rmsnorm_fwd(x, w, y, rstd, eps=eps, stream=stream)()
+
+
+def prepare_rmsnorm_fwd(x, w, y, rstd=None, *, eps: float = 1e-6, stream=None):
     torch = _torch()
     lib = load_library()
     M, N = x.shape
     _expect(w, x.dtype, (N,), "w")
     _expect(y, x.dtype, (M, N), "y")
     _expect(rstd, torch.float32, (M,), "rstd")
-    status = lib.rnq_rmsnorm_fwd(_ptr(x), _ptr(w), _ptr(y), _ptr(rstd), M, N, eps, _dtype_code(x), _stream(x, stream))
-    _check(status)
+    args = (_ptr(x), _ptr(w), _ptr(y), _ptr(rstd), M, N, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_fwd, args)
 
 
 def rnq_rmsnorm_bwd_workspace_size(M: int, N: int) -> int:
@@ -225,6 +253,10 @@ def rnq_rmsnorm_bwd_workspace_size(M: int, N: int) -> int:
 
 
 def rnq_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, eps: float = 1e-6, stream=None) -> None:
+    prepare_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd, eps=eps, stream=stream)()
+
+
+def prepare_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, eps: float = 1e-6, stream=None):
     torch = _torch()
     lib = load_library()
     M, N = x.shape
@@ -234,9 +266,9 @@ def rnq_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, eps: 
     _expect(grad_w, torch.float32, (N,), "grad_w")
     _expect(rstd, torch.float32, (M,), "rstd")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    status = lib.rnq_rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(grad_y), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
-                                 _ptr(workspace), ws_bytes, M, N, eps, _dtype_code(x), _stream(x, stream))
-    _check(status)
+    args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
+            _ptr(workspace), ws_bytes, M, N, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_bwd, args)
 
 
 # ------------------------------------------------------- allocating wrappers

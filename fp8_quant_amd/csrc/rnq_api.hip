@@ -38,23 +38,6 @@ static rnq_status hip_status(hipError_t e, const char* what) {
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-static uint32_t env_u32(const char* name, uint32_t dflt) {
-  const char* v = getenv(name);
-  if (v == nullptr || *v == 0) return dflt;
-  long x = strtol(v, nullptr, 10);
-  return x > 0 ? (uint32_t)x : dflt;
-}
-
-uint32_t tuning_target_waves() {
-  static const uint32_t v = env_u32("RNQ_TARGET_WAVES", 4096);
-  return v;
-}
-
-uint32_t tuning_passes_per_wave() {
-  static const uint32_t v = env_u32("RNQ_PASSES_PER_WAVE", 0);
-  return v;
-}
-
 static bool row_width_ok(int64_t n) { return n == 64 || n == 128 || n == 256 || n == 512; }
 
 static rnq_status check_eps(float eps) {

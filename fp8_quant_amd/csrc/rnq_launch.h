@@ -34,7 +34,6 @@ struct RowParams {
   float scale_floor;   // RN(1e-4 / fp8_max)
   uint32_t scale_by_rcp;
   uint32_t passes;
-  uint32_t passes_per_wave;
   uint32_t div_magic;
   uint32_t div_shift;
 };
@@ -71,9 +70,5 @@ struct WideBwdParams {
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);
 hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream);
-
-// Launch-shape knobs (environment, read once): RNQ_TARGET_WAVES, RNQ_PASSES_PER_WAVE.
-uint32_t tuning_target_waves();
-uint32_t tuning_passes_per_wave();
 
 }  // namespace rnq

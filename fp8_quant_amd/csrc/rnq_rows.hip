@@ -14,7 +14,7 @@
 //    wave covers G = 64/L rows per "pass". Per-row work (reductions, rstd,
 //    scale) runs once per lane for its 16*UPL elements, so a wider share per
 //    lane means less of that work per element.
-//  * A workgroup (4 waves) owns 4*PPW consecutive passes of the flattened
+//  * A workgroup (RW waves) owns RW*PPW consecutive passes of the flattened
 //    (token, head) rows; every wave issues the global loads of all its passes
 //    first, then the workgroup stages the two weight vectors (as fp32) and,
 //    when a token spans at least one pass, the cos/sin rows of the tokens it
@@ -30,8 +30,11 @@
 
 namespace rnq {
 
-constexpr int RT = 256;  // threads per workgroup
-constexpr int RW = RT / 64;
+#ifndef RNQ_ROWS_WAVES
+#define RNQ_ROWS_WAVES 4
+#endif
+constexpr int RW = RNQ_ROWS_WAVES;  // waves per workgroup
+constexpr int RT = 64 * RW;
 
 struct Lane {
   uint32_t row;   // flattened (token, head) index (clamped into range)
@@ -259,17 +262,24 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 
 // --------------------------------------------------------------- launcher
 
-#ifndef RNQ_ROWS_PPW
-#define RNQ_ROWS_PPW 2
-#endif
-constexpr int kPPW = RNQ_ROWS_PPW;  // passes per wave
+// Passes per wave: one pass keeps the smallest unit of work (best balance for
+// launches of a few tens of thousands of passes); two passes amortise the
+// per-wave setup once there are many workgroups per CU.
+constexpr uint32_t kTwoPassesFrom = 1u << 18;  // passes in the launch
 
 template <class DT, int L, int UPL, bool QUANT, bool CLAMP>
-static hipError_t launch_shape(const RowParams& p, bool tbl_lds, dim3 grid, size_t lds, hipStream_t s) {
-  if (tbl_lds)
-    hipLaunchKernelGGL((rows_kernel<DT, L, UPL, kPPW, QUANT, CLAMP, true>), grid, dim3(RT), lds, s, p);
-  else
-    hipLaunchKernelGGL((rows_kernel<DT, L, UPL, kPPW, QUANT, CLAMP, false>), grid, dim3(RT), lds, s, p);
+static hipError_t launch_shape(const RowParams& p, int ppw, bool tbl_lds, dim3 grid, size_t lds, hipStream_t s) {
+  if (ppw == 2) {
+    if (tbl_lds)
+      hipLaunchKernelGGL((rows_kernel<DT, L, UPL, 2, QUANT, CLAMP, true>), grid, dim3(RT), lds, s, p);
+    else
+      hipLaunchKernelGGL((rows_kernel<DT, L, UPL, 2, QUANT, CLAMP, false>), grid, dim3(RT), lds, s, p);
+  } else {
+    if (tbl_lds)
+      hipLaunchKernelGGL((rows_kernel<DT, L, UPL, 1, QUANT, CLAMP, true>), grid, dim3(RT), lds, s, p);
+    else
+      hipLaunchKernelGGL((rows_kernel<DT, L, UPL, 1, QUANT, CLAMP, false>), grid, dim3(RT), lds, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -277,12 +287,12 @@ static hipError_t launch_shape(const RowParams& p, bool tbl_lds, dim3 grid, size
 // row, so each wave-wide access covers whole 128-byte (input) / 64-byte
 // (codes) spans of 8 rows.
 template <class DT, bool QUANT, bool CLAMP>
-static hipError_t launch_dt(const RowParams& p, int D, bool tbl_lds, dim3 grid, size_t lds, hipStream_t s) {
+static hipError_t launch_dt(const RowParams& p, int D, int ppw, bool tbl_lds, dim3 grid, size_t lds, hipStream_t s) {
   switch (D) {
-    case 64: return launch_shape<DT, 4, 1, QUANT, CLAMP>(p, tbl_lds, grid, lds, s);
-    case 128: return launch_shape<DT, 8, 1, QUANT, CLAMP>(p, tbl_lds, grid, lds, s);
-    case 256: return launch_shape<DT, 16, 1, QUANT, CLAMP>(p, tbl_lds, grid, lds, s);
-    case 512: return launch_shape<DT, 32, 1, QUANT, CLAMP>(p, tbl_lds, grid, lds, s);
+    case 64: return launch_shape<DT, 4, 1, QUANT, CLAMP>(p, ppw, tbl_lds, grid, lds, s);
+    case 128: return launch_shape<DT, 8, 1, QUANT, CLAMP>(p, ppw, tbl_lds, grid, lds, s);
+    case 256: return launch_shape<DT, 16, 1, QUANT, CLAMP>(p, ppw, tbl_lds, grid, lds, s);
+    case 512: return launch_shape<DT, 32, 1, QUANT, CLAMP>(p, ppw, tbl_lds, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -309,15 +319,15 @@ static int lanes_per_row(int D) { return D / 16; }
 
 hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStream_t stream) {
   const uint32_t G = 64u / (uint32_t)lanes_per_row(head_dim);
-  const uint32_t rows_per_block = RW * kPPW * G;  // 4 waves x PPW passes x G rows
   p.passes = (uint32_t)((p.total_rows + G - 1) / G);
+  const int ppw = p.passes >= kTwoPassesFrom ? 2 : 1;
+  const uint32_t rows_per_block = RW * (uint32_t)ppw * G;  // waves x passes x rows per pass
   // t = row / heads by multiply-shift: shift = 31 + ceil(log2 heads), magic = ceil(2^shift / heads);
   // exact for every row < 2^31.
   uint32_t lg = 0;
   while ((1u << lg) < p.heads) ++lg;
   p.div_shift = 31 + lg;
   p.div_magic = (uint32_t)((((uint64_t)1 << p.div_shift) + p.heads - 1) / p.heads);
-  p.passes_per_wave = kPPW;
 
   // table rows through LDS when a token spans at least one pass (rows of a token share them)
   const bool tbl_lds = p.rope > 0 && p.heads >= G;
@@ -331,13 +341,13 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;
   const bool clamp = quant && clamp_needed(p.fp8_max);
   if (bf16) {
-    if (!quant) return launch_dt<BF16, false, false>(p, head_dim, tbl_lds, grid, lds, stream);
-    return clamp ? launch_dt<BF16, true, true>(p, head_dim, tbl_lds, grid, lds, stream)
-                 : launch_dt<BF16, true, false>(p, head_dim, tbl_lds, grid, lds, stream);
+    if (!quant) return launch_dt<BF16, false, false>(p, head_dim, ppw, tbl_lds, grid, lds, stream);
+    return clamp ? launch_dt<BF16, true, true>(p, head_dim, ppw, tbl_lds, grid, lds, stream)
+                 : launch_dt<BF16, true, false>(p, head_dim, ppw, tbl_lds, grid, lds, stream);
   }
-  if (!quant) return launch_dt<F16, false, false>(p, head_dim, tbl_lds, grid, lds, stream);
-  return clamp ? launch_dt<F16, true, true>(p, head_dim, tbl_lds, grid, lds, stream)
-               : launch_dt<F16, true, false>(p, head_dim, tbl_lds, grid, lds, stream);
+  if (!quant) return launch_dt<F16, false, false>(p, head_dim, ppw, tbl_lds, grid, lds, stream);
+  return clamp ? launch_dt<F16, true, true>(p, head_dim, ppw, tbl_lds, grid, lds, stream)
+               : launch_dt<F16, true, false>(p, head_dim, ppw, tbl_lds, grid, lds, stream);
 }
 
 }  // namespace rnq

@@ -267,8 +267,7 @@ static int chunks_per_lane(uint32_t N) {
 
 hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream) {
   const int kc = chunks_per_lane(p.N);
-  uint32_t blocks = tuning_target_waves() / WW;
-  if (blocks == 0) blocks = 1;
+  uint32_t blocks = 2048;  // 8 workgroups per CU; each walks rows with a grid stride
   if (blocks > p.M) blocks = p.M;
   dim3 grid(blocks), block(WT);
   return bf16 ? fwd_kc<BF16>(p, kc, grid, block, stream) : fwd_kc<F16>(p, kc, grid, block, stream);
