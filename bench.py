@@ -33,6 +33,7 @@ KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.hip", "fp8_quant_amd/csrc/rnq_dev
                   "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
 ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
+COPY_BYTES = 256 * 2**20  # size of the plain copy used to calibrate the HBM byte counters
 
 
 def kernel_source_hash() -> str:
@@ -211,7 +212,25 @@ def main() -> int:
     ap.add_argument("--workload", default="qk_4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-paths", action="store_true", help="time only the headline workload")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 256 MiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+
+        # three sources, each evicted from the 256 MB Infinity Cache by 1 GiB of
+        # other writes before it is copied, so every copy reads from HBM
+        srcs = [torch.full((COPY_BYTES,), 7 + i, dtype=torch.uint8, device="cuda:0") for i in range(3)]
+        dst = torch.empty_like(srcs[0])
+        scratch = torch.empty((4 * COPY_BYTES,), dtype=torch.uint8, device="cuda:0")
+        for a in srcs:
+            scratch.fill_(1)
+            torch.cuda.synchronize()
+            dst.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

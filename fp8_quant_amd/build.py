@@ -69,5 +69,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_test_programs(verbose: bool = False) -> list:
+    """Test-only HIP programs under tests/csrc (built next to the tests in tests/bin)."""
+    cc = hipcc()
+    src_dir = os.path.join(ROOT, "tests", "csrc")
+    out_dir = os.path.join(ROOT, "tests", "bin")
+    os.makedirs(out_dir, exist_ok=True)
+    built = []
+    for name in ("row_scalar_check",):
+        exe = os.path.join(out_dir, name)
+        cmd = [cc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], "-I", INCLUDE, "-I", CSRC,
+               os.path.join(src_dir, name + ".hip"), "-o", exe]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        built.append(exe)
+    return built
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_test_programs(verbose="-v" in sys.argv))

@@ -1,0 +1,150 @@
+"""Summaries of rocprofv3 output for the measurement record (host-side only).
+
+* ``stats``   - per-kernel call count and durations from a ``--kernel-trace``
+  run (``*_kernel_trace.csv``), as a short Markdown table;
+* ``traffic`` - HBM bytes per launch of the row kernel from two ``--pmc``
+  passes (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled
+  by what the same counter reads for a plain copy of known size, written as
+  JSON together with a hash of the kernel sources (the bench reports the
+  figure only while the sources are unchanged).
+
+Usage::
+
+    python -m fp8_quant_amd.profiling stats TRACE_CSV OUT_MD --command "..."
+    python -m fp8_quant_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV \
+        COPY_BYTES OUT_JSON --kernel rows_kernel --grid 1310720 --command "..."
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_stats(trace_csv: str) -> list[dict]:
+    rows = _rows(trace_csv)
+    by = {}
+    for r in rows:
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        key = (r["Kernel_Name"], r.get("Grid_Size_X") or r.get("Grid_Size", ""))
+        by.setdefault(key, []).append(d)
+    out = []
+    for (name, grid), ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append({
+            "kernel": name, "grid": grid, "calls": len(ds), "avg_ns": sum(ds) / len(ds),
+            "median_ns": statistics.median(ds), "min_ns": min(ds), "max_ns": max(ds), "total_ns": sum(ds),
+        })
+    return out
+
+
+def counter_per_dispatch(counter_csv: str, counter: str, kernel_sub: str, grid: str | None = None) -> float:
+    vals = {}
+    for r in _rows(counter_csv):
+        if r["Counter_Name"] != counter or kernel_sub not in r["Kernel_Name"]:
+            continue
+        g = r.get("Grid_Size") or r.get("Grid_Size_X")
+        if grid is not None and g != grid:
+            continue
+        # a dispatch may report one row per agent-level instance; add them per dispatch
+        vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise ValueError(f"no {counter} rows for kernel matching {kernel_sub!r} (grid {grid})")
+    return statistics.median(vals.values())
+
+
+def write_stats_md(trace_csv: str, out_md: str, command: str, top: int = 12) -> None:
+    st = kernel_stats(trace_csv)
+    lines = [
+        "# rocprofv3 kernel trace summary",
+        "",
+        f"Command: `{command}`",
+        "",
+        "| kernel | grid | calls | avg us | median us | min us | max us |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for s in st[:top]:
+        name = s["kernel"].replace("|", "\\|")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {s['grid']} | {s['calls']} | {s['avg_ns'] / 1e3:.2f} | "
+                     f"{s['median_ns'] / 1e3:.2f} | {s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_traffic_json(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out_json,
+                       kernel_sub, grid, command, algorithmic_bytes=None) -> dict:
+    sys.path.insert(0, ROOT)
+    import bench  # the kernel-source hash the bench compares against
+
+    fetch_kib = counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_sub, grid)
+    write_kib = counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_sub, grid)
+    cf = counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copy", None)
+    cw = counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copy", None)
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    rec = {
+        "kernel": kernel_sub,
+        "grid": grid,
+        "command": command,
+        "fetch_kib_per_dispatch": fetch_kib,
+        "write_kib_per_dispatch": write_kib,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "fetch_bytes_per_launch": round(fetch_b),
+        "write_bytes_per_launch": round(write_b),
+        "traffic_bytes_per_launch": round(fetch_b + write_b),
+        "algorithmic_bytes_per_launch": algorithmic_bytes,
+        "kernel_source_sha256": bench.kernel_source_hash(),
+    }
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("trace_csv")
+    a.add_argument("out_md")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    for n in ("fetch_csv", "write_csv", "copy_fetch_csv", "copy_write_csv"):
+        b.add_argument(n)
+    b.add_argument("copy_bytes", type=int)
+    b.add_argument("out_json")
+    b.add_argument("--kernel", default="rows_kernel")
+    b.add_argument("--grid", default=None)
+    b.add_argument("--algorithmic-bytes", type=int, default=None)
+    b.add_argument("--command", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        write_stats_md(args.trace_csv, args.out_md, args.command)
+    else:
+        rec = write_traffic_json(args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv,
+                                 args.copy_bytes, args.out_json, args.kernel, args.grid, args.command,
+                                 args.algorithmic_bytes)
+        print(json.dumps(rec, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
