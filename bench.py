@@ -29,8 +29,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, QK-norm+RoPE+FP8 4096tok×40h×128"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.hip", "fp8_quant_amd/csrc/rnq_device.h",
-                  "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
+KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.h", "fp8_quant_amd/csrc/rnq_rows_inst.h",
+                  "fp8_quant_amd/csrc/rnq_rows.hip", "fp8_quant_amd/csrc/rnq_rows_quant.hip",
+                  "fp8_quant_amd/csrc/rnq_device.h", "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
 ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
 COPY_BYTES = 256 * 2**20  # size of the plain copy used to calibrate the HBM byte counters
@@ -244,6 +245,9 @@ def main() -> int:
     from fp8_quant_amd import ledger
 
     torch.cuda.set_device(0)
+    # every launch and event goes to one created stream (default priority): the
+    # legacy null stream adds about a microsecond of synchronisation per launch
+    torch.cuda.set_stream(torch.cuda.Stream(device=0))
     head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup)
     wl = workloads.WORKLOADS[args.workload]
     ms = head["ms"]

@@ -82,6 +82,35 @@ const char* rnq_last_error(void) { return g_last_error.c_str(); }
 
 int rnq_abi_version(void) { return 100; }
 
+// One row-kernel launch over tensor 0 (heads0 heads per token) and tensor 1
+// (heads1 heads per token), rows in token-major order.
+static hipError_t launch_qk(const void* x0, const void* w0, uint8_t* c0, float* s0, void* y0, const void* x1,
+                            const void* w1, uint8_t* c1, float* s1, void* y1, const float* cos, const float* sin,
+                            int64_t tokens, int64_t heads0, int64_t heads1, int64_t head_dim, int64_t rope_dim,
+                            float eps, float fp8_max, int dtype, hipStream_t stream) {
+  RowParams p = {};
+  p.x0 = (const uint16_t*)x0;
+  p.w0 = (const uint16_t*)w0;
+  p.c0 = c0;
+  p.s0 = s0;
+  p.y0 = (uint16_t*)y0;
+  p.x1 = (const uint16_t*)x1;
+  p.w1 = (const uint16_t*)w1;
+  p.c1 = c1;
+  p.s1 = s1;
+  p.y1 = (uint16_t*)y1;
+  p.cos = cos;
+  p.sin = sin;
+  p.rstd = nullptr;
+  p.total_rows = (uint32_t)(tokens * (heads0 + heads1));
+  p.heads = (uint32_t)(heads0 + heads1);
+  p.heads0 = (uint32_t)heads0;
+  p.rope = (uint32_t)rope_dim;
+  p.eps = eps;
+  p.fp8_max = fp8_max;
+  return launch_rows(p, (int)head_dim, dtype == RNQ_BF16, true, stream);
+}
+
 rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, const void* wk,
                                 const float* cos, const float* sin,
                                 uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
@@ -112,28 +141,23 @@ rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, co
   if (!aligned(q_fp8, 8) || !aligned(k_fp8, 8)) return fail(RNQ_ERR_UNSUPPORTED, "fp8 outputs must be 8-byte aligned");
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4)) return fail(RNQ_ERR_UNSUPPORTED, "scale outputs must be 4-byte aligned");
 
-  RowParams p = {};
+  const hipStream_t st = (hipStream_t)stream;
+  if (q_heads > 0 && kv_heads > 0 && (q_y == nullptr) != (k_y == nullptr)) {
+    // y for one tensor only: one launch per tensor, so that each launch writes y for all its rows or none
+    hipError_t e = launch_qk(q, wq, q_fp8, q_scale, q_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin,
+                             tokens, q_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+    if (e == hipSuccess)
+      e = launch_qk(k, wk, k_fp8, k_scale, k_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin,
+                    tokens, kv_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+    return hip_status(e, "rnq_qk_norm_rope_fp8");
+  }
   const bool q_first = q_heads > 0;  // tensor 0 is q unless there are no q heads
-  p.x0 = (const uint16_t*)(q_first ? q : k);
-  p.w0 = (const uint16_t*)(q_first ? wq : wk);
-  p.c0 = q_first ? q_fp8 : k_fp8;
-  p.s0 = q_first ? q_scale : k_scale;
-  p.y0 = (uint16_t*)(q_first ? q_y : k_y);
-  p.x1 = (const uint16_t*)(q_first ? k : nullptr);
-  p.w1 = (const uint16_t*)(q_first ? wk : nullptr);
-  p.c1 = q_first ? k_fp8 : nullptr;
-  p.s1 = q_first ? k_scale : nullptr;
-  p.y1 = (uint16_t*)(q_first ? k_y : nullptr);
-  p.cos = cos;
-  p.sin = sin;
-  p.rstd = nullptr;
-  p.total_rows = (uint32_t)rows;
-  p.heads = (uint32_t)heads;
-  p.heads0 = (uint32_t)(q_first ? q_heads : kv_heads);
-  p.rope = (uint32_t)rope_dim;
-  p.eps = eps;
-  p.fp8_max = fp8_max;
-  return hip_status(launch_rows(p, (int)head_dim, dtype == RNQ_BF16, true, (hipStream_t)stream), "rnq_qk_norm_rope_fp8");
+  const hipError_t e =
+      q_first ? launch_qk(q, wq, q_fp8, q_scale, q_y, k, wk, k_fp8, k_scale, k_y, cos, sin, tokens, q_heads, kv_heads,
+                          head_dim, rope_dim, eps, fp8_max, dtype, st)
+              : launch_qk(k, wk, k_fp8, k_scale, k_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin, tokens,
+                          kv_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+  return hip_status(e, "rnq_qk_norm_rope_fp8");
 }
 
 rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,

@@ -20,7 +20,7 @@ struct RowParams {
   uint8_t* c1;
   float* s0;    // scales
   float* s1;
-  uint16_t* y0;  // optional y (both or neither)
+  uint16_t* y0;  // optional y (for both tensors or for neither)
   uint16_t* y1;
   float* rstd;   // optional per-row rstd, flattened row order
   uint32_t total_rows;
@@ -33,9 +33,20 @@ struct RowParams {
   float rcp_fp8_max;   // RN(1 / fp8_max)
   float scale_floor;   // RN(1e-4 / fp8_max)
   uint32_t scale_by_rcp;
-  uint32_t passes;
+  uint32_t clamp;       // clamp quotients to +-fp8_max before encoding
+  uint32_t passes;      // groups of 64 / (D / 16) consecutive rows
+  uint32_t waves;       // waves that take passes (round-robin)
+  uint32_t per_wave;    // passes per wave (the last ones repeat the final pass)
   uint32_t div_magic;
   uint32_t div_shift;
+};
+
+// What a row-kernel launch computes and writes (bit set).
+enum RowMode : int {
+  ROW_QUANT = 1,  // fp8 codes + per-row scale
+  ROW_ROPE = 2,   // rotate the rope tail
+  ROW_Y = 4,      // write y (16-bit)
+  ROW_RSTD = 8,   // write per-row rstd
 };
 
 hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStream_t stream);

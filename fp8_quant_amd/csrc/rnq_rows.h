@@ -1,0 +1,328 @@
+// Row kernel: RMSNorm -> partial NeoX RoPE -> (optional) per-row FP8 e4m3fn.
+//
+// Operation: tilelang-tutorial chapter 13 fusion page, torch_reference_fused
+// and the two fused kernels; chapter 28 case study, the QK-norm prologue
+// (rows are (token, head) pairs; every head of a token uses the token's
+// cos/sin row; one fp32 scale per row).
+//
+// Mapping (gfx950, wave64).
+//  * A row of D = 16*L elements is split into L "units" of two 16-byte chunks,
+//    one unit per lane: a rope unit holds chunk j of the lower half of the
+//    rope tail and chunk j of the upper half (the lane owns both members of
+//    its 8 RoPE pairs, so no exchange is needed); a plain unit holds two
+//    adjacent chunks. A wave covers G = 64/L rows per "pass"; each wave-wide
+//    load covers whole 128-byte spans of 8 rows (D = 128).
+//  * W waves take the passes round-robin (wave w takes w, w + W, w + 2W, ...),
+//    so the waves in flight work on one narrow window of the tensors and DRAM
+//    pages are used whole. W is about what stays resident, or more for large
+//    launches (at most 8 passes per wave; later waves start in launch order as
+//    earlier ones retire). Every wave runs the same number of passes; the few
+//    slots past the end repeat the final pass, which writes the same bytes
+//    again.
+//  * Software pipeline: the input chunks of the next NS - 1 passes and the
+//    cos/sin values of the next pass are in flight while a pass is computed.
+//    No memory access in the steady state is conditional (clamped indices,
+//    every lane of a row storing the same scale), so the in-order memory
+//    counter can be waited on precisely.
+//  * When every pass stays inside one token and one tensor (heads and q heads
+//    both multiples of G, the usual QK layout), a pass's token and tensor are
+//    wave-uniform and its addresses are one scalar base plus lane-constant
+//    offsets. Otherwise each lane locates its own row.
+//  * The two weight vectors are staged once per workgroup in LDS (fp32).
+//  * Row sums: sum of squares in fp64 (exact for 16-bit inputs) and the
+//    absmax, each reduced over the L lanes with DPP.
+//  * Workgroups are renumbered so that neighbouring row ranges (which share
+//    tokens) run on the same XCD and its L2.
+#pragma once
+
+#include <math.h>
+
+#include "rnq_device.h"
+#include "rnq_launch.h"
+
+namespace rnq {
+
+constexpr int RW = 4;  // waves per workgroup
+constexpr int RT = 64 * RW;
+
+#ifndef RNQ_ROWS_CHUNKED
+#define RNQ_ROWS_CHUNKED 0
+#endif
+#ifndef RNQ_ROWS_STAGES
+#define RNQ_ROWS_STAGES 2
+#endif
+constexpr int NS = RNQ_ROWS_STAGES;  // passes of input in flight per wave, plus the one in use
+static_assert(NS >= 2 && NS % 2 == 0, "the table ring alternates between two buffers");
+
+// Where one lane's row of a pass lives.
+struct Loc {
+  uint32_t row;   // flattened (token, head) index (clamped into range)
+  uint32_t tok;
+  uint32_t ri;    // row index inside its tensor
+  uint32_t ri0;   // aligned passes: row index of the pass's first row (wave-uniform)
+  bool second;    // row of tensor 1 (k)
+};
+
+// A pass's input chunks and its cos/sin values.
+struct Data {
+  Loc loc;
+  uint4 xa, xb;
+};
+struct Table {
+  float4 c0, c1, s0, s1;
+};
+
+__device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) {
+  return (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);  // row / heads, exact below 2^31
+}
+
+template <int G, bool ALIGNED>
+__device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_t slot) {
+  Loc r;
+  if constexpr (ALIGNED) {
+    // the whole pass lies inside one token and one tensor, and the launch
+    // holds whole passes only: everything but the slot is wave-uniform
+    const uint32_t row0 = pass * (uint32_t)G;
+    const uint32_t t = div_heads(p, row0);
+    const uint32_t h0 = row0 - t * p.heads;
+    r.second = h0 >= p.heads0;
+    const uint32_t ri0 = r.second ? t * (p.heads - p.heads0) + (h0 - p.heads0) : t * p.heads0 + h0;
+    r.tok = t;
+    r.ri0 = ri0;
+    r.ri = ri0 + slot;
+    r.row = row0 + slot;
+  } else {
+    // rows past the end repeat the last row (same inputs, same bytes written)
+    const uint32_t row = min(pass * (uint32_t)G + slot, p.total_rows - 1);
+    r.row = row;
+    const uint32_t t = div_heads(p, row);
+    const uint32_t h = row - t * p.heads;
+    r.tok = t;
+    r.second = h >= p.heads0;
+    r.ri = r.second ? t * (p.heads - p.heads0) + (h - p.heads0) : t * p.heads0 + h;
+    r.ri0 = 0;
+  }
+  return r;
+}
+
+template <class DT, int L, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
+  constexpr bool QUANT = (MODE & ROW_QUANT) != 0;
+  constexpr bool ROPE = (MODE & ROW_ROPE) != 0;
+  constexpr bool WY = (MODE & ROW_Y) != 0;
+  constexpr bool WR = (MODE & ROW_RSTD) != 0;
+  constexpr int D = 16 * L;
+  constexpr int G = 64 / L;
+  __shared__ float w_lds[2 * D];
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t u = lane % L;
+  const uint32_t slot = lane / L;
+
+  // XCD-aware renumbering: hardware places workgroup b on XCD b % 8; give the
+  // workgroups of one XCD a contiguous stretch of the wave numbers.
+  uint32_t blk = blockIdx.x;
+  {
+    const uint32_t nb = gridDim.x, full = nb & ~7u;
+    if (blk < full) blk = (blk & 7u) * (full >> 3) + (blk >> 3);
+  }
+  const uint32_t gw = blk * RW + wave;
+  const uint32_t W = p.waves, n = p.per_wave, last = p.passes - 1;
+  // (waves past p.waves, at most RW - 1, load clamped passes and leave after the barrier)
+#if RNQ_ROWS_CHUNKED
+  auto pass_of = [&](uint32_t i) { return min(gw * n + i, last); };
+#else
+  auto pass_of = [&](uint32_t i) { return min(gw + i * W, last); };
+#endif
+
+  // ---- this lane's columns
+  const uint32_t R = ROPE ? p.rope : 0u, half = R / 2;
+  const uint32_t n_plain = (D - R) / 16;  // units outside the rope tail
+  const bool rope_lane = u >= n_plain;
+  uint32_t off_a, off_b, cs_off;
+  if (!rope_lane) {
+    off_a = 16 * u;
+    off_b = off_a + 8;
+    cs_off = 0;
+  } else {
+    const uint32_t j = u - n_plain;
+    off_a = (D - R) + 8 * j;
+    off_b = off_a + half;
+    cs_off = 8 * j;
+  }
+  // aligned passes: element offsets of this lane's chunks from the pass's first row
+  const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
+
+  auto load_data = [&](Data& d, uint32_t pass) {
+    d.loc = locate<G, ALIGNED>(p, pass, slot);
+    if constexpr (ALIGNED) {
+      // one wave-uniform base, lane offsets below 2^32 bytes
+      const char* base = (const char*)((d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri0 * D);
+      d.xa = load_stream16(base + 2u * pe_a);
+      d.xb = load_stream16(base + 2u * pe_b);
+    } else {
+      const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri * D;
+      d.xa = load_stream16(src + off_a);
+      d.xb = load_stream16(src + off_b);
+    }
+  };
+  // every lane loads (plain lanes read the row start and ignore it)
+  auto load_table = [&](Table& t, const Loc& r) {
+    if constexpr (ROPE) {
+      // token row base (wave-uniform for aligned passes) plus the lane's byte offset
+      const char* cp = (const char*)(p.cos + (size_t)r.tok * half) + 4u * cs_off;
+      const char* sp = (const char*)(p.sin + (size_t)r.tok * half) + 4u * cs_off;
+      t.c0 = *(const float4*)cp;
+      t.c1 = *(const float4*)(cp + 16);
+      t.s0 = *(const float4*)sp;
+      t.s1 = *(const float4*)(sp + 16);
+    }
+  };
+
+  auto compute = [&](const Data& s, const Table& t) {
+    const Loc& r = s.loc;
+    const float* w = w_lds + (r.second ? D : 0);
+
+    // ---- sum of squares: fp64 (exact for 16-bit inputs), reduced over the row's lanes
+    float xv[16];
+    unpack8<DT>(s.xa, xv);
+    unpack8<DT>(s.xb, xv + 8);
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc = __builtin_fma((double)xv[e], (double)xv[e], acc);
+    acc = group_sum<L>(acc);
+    const float ssq = (float)acc;               // one rounding of the exact sum
+    const float ms = ssq * (1.0f / (float)D);   // D is a power of two: equals ssq / D
+    const float rstd = rstd_of(ms + p.eps);
+
+    // ---- normalise: (x * rstd) * w, rounded to the input dtype
+    const float4 wa0 = *(const float4*)(w + off_a), wa1 = *(const float4*)(w + off_a + 4);
+    const float4 wb0 = *(const float4*)(w + off_b), wb1 = *(const float4*)(w + off_b + 4);
+    const float wv[16] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w,
+                          wb0.x, wb0.y, wb0.z, wb0.w, wb1.x, wb1.y, wb1.z, wb1.w};
+    float n[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) n[e] = (xv[e] * rstd) * wv[e];
+    uint4 ya = pack8<DT>(n);
+    uint4 yb = pack8<DT>(n + 8);
+
+    // ---- RoPE on the tail: lo' = lo c - hi s, hi' = hi c + lo s, each rounded to dtype
+    if constexpr (ROPE) {
+      if (rope_lane) {
+        const float cc[8] = {t.c0.x, t.c0.y, t.c0.z, t.c0.w, t.c1.x, t.c1.y, t.c1.z, t.c1.w};
+        const float ss[8] = {t.s0.x, t.s0.y, t.s0.z, t.s0.w, t.s1.x, t.s1.y, t.s1.z, t.s1.w};
+        float lo[8], hi[8], ra[8], rb[8];
+        unpack8<DT>(ya, lo);
+        unpack8<DT>(yb, hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ra[e] = (lo[e] * cc[e]) - (hi[e] * ss[e]);
+          rb[e] = (hi[e] * cc[e]) + (lo[e] * ss[e]);
+        }
+        ya = pack8<DT>(ra);
+        yb = pack8<DT>(rb);
+      }
+    }
+
+    // element offsets: aligned passes from a wave-uniform row base, else from the tensor start
+    const size_t rbase = ALIGNED ? (size_t)r.ri0 * D : (size_t)r.ri * D;
+    const uint32_t ea = ALIGNED ? pe_a : off_a, eb = ALIGNED ? pe_b : off_b;
+    if constexpr (WY) {
+      char* dst = (char*)((r.second ? p.y1 : p.y0) + rbase);
+      *(uint4*)(dst + 2u * ea) = ya;
+      *(uint4*)(dst + 2u * eb) = yb;
+    }
+    // every lane of the row stores the same value
+    if constexpr (WR) p.rstd[r.row] = rstd;
+
+    if constexpr (QUANT) {
+      float yv[16];
+      unpack8<DT>(ya, yv);
+      unpack8<DT>(yb, yv + 8);
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(yv[e]));
+      const float amax = group_max<L>(m);
+      // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
+      float scale;
+      if (p.scale_by_rcp)
+        scale = amax >= 1e-4f ? div_by(amax, p.fp8_max, p.rcp_fp8_max) : p.scale_floor;
+      else
+        scale = fmaxf(amax, 1e-4f) / p.fp8_max;
+      const float rs = rcp_rn(scale);
+      float q[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) q[e] = div_by(yv[e], scale, rs);
+      if (p.clamp) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -p.fp8_max, p.fp8_max);
+      }
+      uint2 ca, cb;
+      ca.x = fp8x4(q[0], q[1], q[2], q[3], ya.x);
+      ca.y = fp8x4(q[4], q[5], q[6], q[7], ya.y);
+      cb.x = fp8x4(q[8], q[9], q[10], q[11], yb.x);
+      cb.y = fp8x4(q[12], q[13], q[14], q[15], yb.y);
+      uint8_t* cdst = (r.second ? p.c1 : p.c0) + rbase;
+      store_stream8(cdst + ea, ca);
+      store_stream8(cdst + eb, cb);
+      float* sdst = r.second ? p.s1 : p.s0;
+      if constexpr (ALIGNED)
+        sdst[r.ri0 + slot] = scale;  // every lane of the row stores the same value
+      else
+        sdst[r.ri] = scale;
+    }
+  };
+
+  // ---- software pipeline over this wave's n passes: input NS - 1 passes
+  // ahead, table values one pass ahead (ring slots are compile-time indices).
+  // The first loads go out before the weights are staged.
+  Data d[NS];
+  Table tb[2];
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) load_data(d[k], pass_of(k));
+  load_table(tb[0], d[0].loc);
+
+  // ---- weights of both tensors, fp32, in LDS (every thread loads a chunk, so
+  // that no global access is conditional; the first D / 8 threads store them)
+  {
+    const uint32_t c = tid % (D / 8);
+    const uint4 w0c = *(const uint4*)(p.w0 + 8 * c);
+    const uint4 w1c = *(const uint4*)((p.heads0 < p.heads ? p.w1 : p.w0) + 8 * c);
+    if (tid < D / 8) {
+      float f[8];
+      unpack8<DT>(w0c, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w_lds[8 * tid + i] = f[i];
+      unpack8<DT>(w1c, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w_lds[D + 8 * tid + i] = f[i];
+    }
+  }
+  __syncthreads();
+  if (gw >= W) return;
+
+  uint32_t base = 0;
+  for (; base + NS <= n; base += NS) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
+      load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
+      compute(d[k], tb[k % 2]);
+    }
+  }
+  // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    if (base + k < n) {
+      if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
+      compute(d[k], tb[k % 2]);
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, bool aligned, dim3 grid, hipStream_t s);
+
+}  // namespace rnq
