@@ -25,6 +25,8 @@ struct BF16 {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
+  // a rounded to bf16, as an fp32 value: one conversion with a zero low half
+  static __device__ __forceinline__ float round(float a) { return __uint_as_float(pack(0.0f, a)); }
 };
 
 struct F16 {
@@ -38,6 +40,14 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  // a rounded to fp16, as an fp32 value. The empty asm pins a as an fp32
+  // value first: otherwise the compiler may fold the product that produced it
+  // into one mixed-precision fma that rounds straight to fp16 (one rounding
+  // where the operation rounds twice).
+  static __device__ __forceinline__ float round(float a) {
+    asm volatile("" : "+v"(a));
+    return (float)(_Float16)a;
   }
 };
 
@@ -73,6 +83,35 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 __device__ __forceinline__ void store_stream8(void* p, uint2 v) {
   const u32x2 w = {v.x, v.y};
   __builtin_nontemporal_store(w, (u32x2*)p);
+}
+
+// Raw buffer accesses: a wave-uniform base (the descriptor, in scalar
+// registers) plus a 32-bit per-lane byte offset, so no per-lane 64-bit address
+// arithmetic. Offsets at or past `bytes` read zero / are dropped by the
+// hardware range check. Dword 3 of the descriptor: raw (untyped) 32-bit data.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // cache-policy bit: streaming access, no reuse
+__device__ __forceinline__ uint4 buf_load16_nt(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 buf_load16f(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8_nt(rsrc_t r, uint32_t off, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
 // ------------------------------------------------------------ DPP reductions

@@ -54,6 +54,13 @@ constexpr int RT = 64 * RW;
 constexpr int NS = RNQ_ROWS_STAGES;  // passes of input in flight per wave, plus the one in use
 static_assert(NS >= 2 && NS % 2 == 0, "the table ring alternates between two buffers");
 
+// Variants of the pass loop chosen once per wave: GEN = per-pass branches for
+// fp8_max below 1 or a clamp that can bind; FULL = the rope tail is the whole row.
+template <bool GEN, bool FULL>
+struct Opts {
+  static constexpr bool gen = GEN, full = FULL;
+};
+
 // Where one lane's row of a pass lives.
 struct Loc {
   uint32_t row;   // flattened (token, head) index (clamped into range)
@@ -158,10 +165,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   auto load_data = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, ALIGNED>(p, pass, slot);
     if constexpr (ALIGNED) {
-      // one wave-uniform base, lane offsets below 2^32 bytes
-      const char* base = (const char*)((d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri0 * D);
-      d.xa = load_stream16(base + 2u * pe_a);
-      d.xb = load_stream16(base + 2u * pe_b);
+      // the pass's G rows: one wave-uniform descriptor, lane byte offsets
+      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri0 * D, 2u * G * D);
+      d.xa = buf_load16_nt(rx, 2u * pe_a);
+      d.xb = buf_load16_nt(rx, 2u * pe_b);
     } else {
       const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri * D;
       d.xa = load_stream16(src + off_a);
@@ -171,17 +178,28 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   // every lane loads (plain lanes read the row start and ignore it)
   auto load_table = [&](Table& t, const Loc& r) {
     if constexpr (ROPE) {
-      // token row base (wave-uniform for aligned passes) plus the lane's byte offset
-      const char* cp = (const char*)(p.cos + (size_t)r.tok * half) + 4u * cs_off;
-      const char* sp = (const char*)(p.sin + (size_t)r.tok * half) + 4u * cs_off;
-      t.c0 = *(const float4*)cp;
-      t.c1 = *(const float4*)(cp + 16);
-      t.s0 = *(const float4*)sp;
-      t.s1 = *(const float4*)(sp + 16);
+      if constexpr (ALIGNED) {
+        // the token's cos and sin rows: wave-uniform descriptors
+        const rsrc_t rc = make_rsrc(p.cos + (size_t)r.tok * half, 4u * half);
+        const rsrc_t rs = make_rsrc(p.sin + (size_t)r.tok * half, 4u * half);
+        t.c0 = buf_load16f(rc, 4u * cs_off);
+        t.c1 = buf_load16f(rc, 4u * cs_off + 16u);
+        t.s0 = buf_load16f(rs, 4u * cs_off);
+        t.s1 = buf_load16f(rs, 4u * cs_off + 16u);
+      } else {
+        const float* cp = p.cos + (size_t)r.tok * half + cs_off;
+        const float* sp = p.sin + (size_t)r.tok * half + cs_off;
+        t.c0 = *(const float4*)cp;
+        t.c1 = *(const float4*)(cp + 4);
+        t.s0 = *(const float4*)sp;
+        t.s1 = *(const float4*)(sp + 4);
+      }
     }
   };
 
-  auto compute = [&](const Data& s, const Table& t) {
+  auto compute = [&](const Data& s, const Table& t, auto opts) {
+    constexpr bool GEN = decltype(opts)::gen;
+    constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
     const Loc& r = s.loc;
     const float* w = w_lds + (r.second ? D : 0);
 
@@ -197,32 +215,26 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     const float ms = ssq * (1.0f / (float)D);   // D is a power of two: equals ssq / D
     const float rstd = rstd_of(ms + p.eps);
 
-    // ---- normalise: (x * rstd) * w, rounded to the input dtype
+    // ---- normalise: (x * rstd) * w, rounded to the input dtype (values kept as fp32)
     const float4 wa0 = *(const float4*)(w + off_a), wa1 = *(const float4*)(w + off_a + 4);
     const float4 wb0 = *(const float4*)(w + off_b), wb1 = *(const float4*)(w + off_b + 4);
     const float wv[16] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w,
                           wb0.x, wb0.y, wb0.z, wb0.w, wb1.x, wb1.y, wb1.z, wb1.w};
-    float n[16];
+    float y[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) n[e] = (xv[e] * rstd) * wv[e];
-    uint4 ya = pack8<DT>(n);
-    uint4 yb = pack8<DT>(n + 8);
+    for (int e = 0; e < 16; ++e) y[e] = DT::round((xv[e] * rstd) * wv[e]);
 
     // ---- RoPE on the tail: lo' = lo c - hi s, hi' = hi c + lo s, each rounded to dtype
     if constexpr (ROPE) {
-      if (rope_lane) {
+      if (FULL || rope_lane) {
         const float cc[8] = {t.c0.x, t.c0.y, t.c0.z, t.c0.w, t.c1.x, t.c1.y, t.c1.z, t.c1.w};
         const float ss[8] = {t.s0.x, t.s0.y, t.s0.z, t.s0.w, t.s1.x, t.s1.y, t.s1.z, t.s1.w};
-        float lo[8], hi[8], ra[8], rb[8];
-        unpack8<DT>(ya, lo);
-        unpack8<DT>(yb, hi);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ra[e] = (lo[e] * cc[e]) - (hi[e] * ss[e]);
-          rb[e] = (hi[e] * cc[e]) + (lo[e] * ss[e]);
+          const float lo = y[e], hi = y[8 + e];
+          y[e] = DT::round((lo * cc[e]) - (hi * ss[e]));
+          y[8 + e] = DT::round((hi * cc[e]) + (lo * ss[e]));
         }
-        ya = pack8<DT>(ra);
-        yb = pack8<DT>(rb);
       }
     }
 
@@ -230,48 +242,57 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     const size_t rbase = ALIGNED ? (size_t)r.ri0 * D : (size_t)r.ri * D;
     const uint32_t ea = ALIGNED ? pe_a : off_a, eb = ALIGNED ? pe_b : off_b;
     if constexpr (WY) {
-      char* dst = (char*)((r.second ? p.y1 : p.y0) + rbase);
-      *(uint4*)(dst + 2u * ea) = ya;
-      *(uint4*)(dst + 2u * eb) = yb;
+      // the values are already rounded: packing them is exact
+      uint16_t* ybase = (r.second ? p.y1 : p.y0) + rbase;
+      if constexpr (ALIGNED) {
+        const rsrc_t ry = make_rsrc(ybase, 2u * G * D);
+        buf_store16(ry, 2u * ea, pack8<DT>(y));
+        buf_store16(ry, 2u * eb, pack8<DT>(y + 8));
+      } else {
+        *(uint4*)((char*)ybase + 2u * ea) = pack8<DT>(y);
+        *(uint4*)((char*)ybase + 2u * eb) = pack8<DT>(y + 8);
+      }
     }
     // every lane of the row stores the same value
     if constexpr (WR) p.rstd[r.row] = rstd;
 
     if constexpr (QUANT) {
-      float yv[16];
-      unpack8<DT>(ya, yv);
-      unpack8<DT>(yb, yv + 8);
       float m = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(yv[e]));
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[e]));
       const float amax = group_max<L>(m);
       // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
       float scale;
-      if (p.scale_by_rcp)
+      if (!GEN || p.scale_by_rcp)
         scale = amax >= 1e-4f ? div_by(amax, p.fp8_max, p.rcp_fp8_max) : p.scale_floor;
       else
         scale = fmaxf(amax, 1e-4f) / p.fp8_max;
       const float rs = rcp_rn(scale);
       float q[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = div_by(yv[e], scale, rs);
-      if (p.clamp) {
+      for (int e = 0; e < 16; ++e) q[e] = div_by(y[e], scale, rs);
+      if (GEN && p.clamp) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -p.fp8_max, p.fp8_max);
       }
       uint2 ca, cb;
-      ca.x = fp8x4(q[0], q[1], q[2], q[3], ya.x);
-      ca.y = fp8x4(q[4], q[5], q[6], q[7], ya.y);
-      cb.x = fp8x4(q[8], q[9], q[10], q[11], yb.x);
-      cb.y = fp8x4(q[12], q[13], q[14], q[15], yb.y);
+      ca.x = fp8x4(q[0], q[1], q[2], q[3], __float_as_uint(q[0]));
+      ca.y = fp8x4(q[4], q[5], q[6], q[7], __float_as_uint(q[4]));
+      cb.x = fp8x4(q[8], q[9], q[10], q[11], __float_as_uint(q[8]));
+      cb.y = fp8x4(q[12], q[13], q[14], q[15], __float_as_uint(q[12]));
       uint8_t* cdst = (r.second ? p.c1 : p.c0) + rbase;
-      store_stream8(cdst + ea, ca);
-      store_stream8(cdst + eb, cb);
       float* sdst = r.second ? p.s1 : p.s0;
-      if constexpr (ALIGNED)
-        sdst[r.ri0 + slot] = scale;  // every lane of the row stores the same value
-      else
+      if constexpr (ALIGNED) {
+        const rsrc_t rq = make_rsrc(cdst, (uint32_t)(G * D));
+        buf_store8_nt(rq, ea, ca);
+        buf_store8_nt(rq, eb, cb);
+        const rsrc_t rsc = make_rsrc(sdst + r.ri0, 4u * G);
+        buf_store4(rsc, 4u * slot, scale);  // every lane of the row stores the same value
+      } else {
+        store_stream8(cdst + ea, ca);
+        store_stream8(cdst + eb, cb);
         sdst[r.ri] = scale;
+      }
     }
   };
 
@@ -303,23 +324,31 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   __syncthreads();
   if (gw >= W) return;
 
-  uint32_t base = 0;
-  for (; base + NS <= n; base += NS) {
+  auto run = [&](auto opts) {
+    uint32_t base = 0;
+    for (; base + NS <= n; base += NS) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
-      load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
-      compute(d[k], tb[k % 2]);
+      for (int k = 0; k < NS; ++k) {
+        load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
+        load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
+        compute(d[k], tb[k % 2], opts);
+      }
     }
-  }
-  // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
+    // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k) {
-    if (base + k < n) {
-      if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
-      compute(d[k], tb[k % 2]);
+    for (int k = 0; k < NS - 1; ++k) {
+      if (base + k < n) {
+        if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
+        compute(d[k], tb[k % 2], opts);
+      }
     }
-  }
+  };
+  if (QUANT && (p.clamp || !p.scale_by_rcp))
+    run(Opts<true, false>{});
+  else if (ROPE && R == (uint32_t)D)
+    run(Opts<false, true>{});
+  else
+    run(Opts<false, false>{});
 }
 
 template <int MODE>
