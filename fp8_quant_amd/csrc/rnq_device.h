@@ -89,13 +89,25 @@ __device__ __forceinline__ void store_stream8(void* p, uint2 v) {
 // registers) plus a 32-bit per-lane byte offset, so no per-lane 64-bit address
 // arithmetic. Offsets at or past `bytes` read zero / are dropped by the
 // hardware range check. Dword 3 of the descriptor: raw (untyped) 32-bit data.
+// The base must be wave-uniform; it is read from the first active lane so
+// that the descriptor is built in scalar registers whatever path the value
+// took (a descriptor the compiler thinks divergent costs a loop per access).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  // (readfirstlane returns int: convert through uint32_t so the low half is
+  // zero-extended, never sign-extended into the high half)
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | (uint64_t)lo), 0, (int)bytes, 0x00020000);
 }
 constexpr int kNonTemporal = 2;  // cache-policy bit: streaming access, no reuse
 __device__ __forceinline__ uint4 buf_load16_nt(rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float4 buf_load16f(rsrc_t r, uint32_t off) {

@@ -76,7 +76,8 @@ struct Data {
   uint4 xa, xb;
 };
 struct Table {
-  float4 c0, c1, s0, s1;
+  float4 c0, c1, s0, s1;  // this lane's values (per-lane rows)
+  uint4 cw, sw;           // one 16-byte chunk of the token's cos and sin rows (aligned passes)
 };
 
 __device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) {
@@ -89,11 +90,14 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
   if constexpr (ALIGNED) {
     // the whole pass lies inside one token and one tensor, and the launch
     // holds whole passes only: everything but the slot is wave-uniform
-    const uint32_t row0 = pass * (uint32_t)G;
-    const uint32_t t = div_heads(p, row0);
+    // (readfirstlane: keep the wave-uniform values in scalar registers through
+    // every control-flow merge, so descriptors built from them stay scalar)
+    const uint32_t row0 = __builtin_amdgcn_readfirstlane(pass * (uint32_t)G);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(div_heads(p, row0));
     const uint32_t h0 = row0 - t * p.heads;
     r.second = h0 >= p.heads0;
-    const uint32_t ri0 = r.second ? t * (p.heads - p.heads0) + (h0 - p.heads0) : t * p.heads0 + h0;
+    const uint32_t ri0 = __builtin_amdgcn_readfirstlane(
+        r.second ? t * (p.heads - p.heads0) + (h0 - p.heads0) : t * p.heads0 + h0);
     r.tok = t;
     r.ri0 = ri0;
     r.ri = ri0 + slot;
@@ -121,6 +125,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr int D = 16 * L;
   constexpr int G = 64 / L;
   __shared__ float w_lds[2 * D];
+  // aligned rope passes: each wave stages the pass's cos and sin rows here
+  constexpr bool STAGED = ALIGNED && ROPE;
+  __shared__ float t_lds[STAGED ? RW * D : 1];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -161,6 +168,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   }
   // aligned passes: element offsets of this lane's chunks from the pass's first row
   const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
+  // aligned rope passes: lane l < half / 4 carries chunk l of the cos row and of the sin row
+  const uint32_t q4 = half / 4, tq = 16u * (q4 ? lane % q4 : 0u);
+  float* t_wave = t_lds + (STAGED ? wave * D : 0);
 
   auto load_data = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, ALIGNED>(p, pass, slot);
@@ -179,13 +189,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   auto load_table = [&](Table& t, const Loc& r) {
     if constexpr (ROPE) {
       if constexpr (ALIGNED) {
-        // the token's cos and sin rows: wave-uniform descriptors
+        // the token's cos and sin rows (wave-uniform descriptors), one chunk
+        // of each per lane; the rows go through LDS to the lanes that use them
         const rsrc_t rc = make_rsrc(p.cos + (size_t)r.tok * half, 4u * half);
         const rsrc_t rs = make_rsrc(p.sin + (size_t)r.tok * half, 4u * half);
-        t.c0 = buf_load16f(rc, 4u * cs_off);
-        t.c1 = buf_load16f(rc, 4u * cs_off + 16u);
-        t.s0 = buf_load16f(rs, 4u * cs_off);
-        t.s1 = buf_load16f(rs, 4u * cs_off + 16u);
+        t.cw = buf_load16(rc, tq);
+        t.sw = buf_load16(rs, tq);
       } else {
         const float* cp = p.cos + (size_t)r.tok * half + cs_off;
         const float* sp = p.sin + (size_t)r.tok * half + cs_off;
@@ -197,7 +206,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     }
   };
 
-  auto compute = [&](const Data& s, const Table& t, auto opts) {
+  // t: this pass's table values; aligned rope passes stage them in LDS and
+  // then load the next pass's table (at `next`) into t.
+  auto compute = [&](const Data& s, Table& t, const Loc& next, auto opts) {
     constexpr bool GEN = decltype(opts)::gen;
     constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
     const Loc& r = s.loc;
@@ -224,11 +235,28 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) y[e] = DT::round((xv[e] * rstd) * wv[e]);
 
+    if constexpr (STAGED) {
+      // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
+      // accesses complete in order, so the reads below see these writes and the
+      // previous pass's reads are done before they land
+      if (lane < q4) {
+        *(uint4*)(t_wave + 4 * lane) = t.cw;
+        *(uint4*)(t_wave + half + 4 * lane) = t.sw;
+      }
+    }
+
     // ---- RoPE on the tail: lo' = lo c - hi s, hi' = hi c + lo s, each rounded to dtype
     if constexpr (ROPE) {
       if (FULL || rope_lane) {
-        const float cc[8] = {t.c0.x, t.c0.y, t.c0.z, t.c0.w, t.c1.x, t.c1.y, t.c1.z, t.c1.w};
-        const float ss[8] = {t.s0.x, t.s0.y, t.s0.z, t.s0.w, t.s1.x, t.s1.y, t.s1.z, t.s1.w};
+        float4 c0 = t.c0, c1 = t.c1, s0 = t.s0, s1 = t.s1;
+        if constexpr (STAGED) {
+          c0 = *(const float4*)(t_wave + cs_off);
+          c1 = *(const float4*)(t_wave + cs_off + 4);
+          s0 = *(const float4*)(t_wave + half + cs_off);
+          s1 = *(const float4*)(t_wave + half + cs_off + 4);
+        }
+        const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lo = y[e], hi = y[8 + e];
@@ -294,6 +322,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
         sdst[r.ri] = scale;
       }
     }
+    // the next pass's table rows go out after this pass's stores: at the next
+    // pass, only that pass's input loads were issued after them
+    if constexpr (STAGED) load_table(t, next);
   };
 
   // ---- software pipeline over this wave's n passes: input NS - 1 passes
@@ -321,6 +352,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       for (int i = 0; i < 8; ++i) w_lds[D + 8 * tid + i] = f[i];
     }
   }
+  // everything loaded so far has landed: the loop then starts from the same
+  // outstanding-access count on every entry, which keeps the compiler's
+  // memory-counter waits inside the loop exact
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (gw >= W) return;
 
@@ -330,16 +365,25 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
-        load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
-        compute(d[k], tb[k % 2], opts);
+        if constexpr (STAGED) {
+          compute(d[k], tb[0], d[(k + 1) % NS].loc, opts);
+        } else {
+          load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
+          compute(d[k], tb[k % 2], d[k].loc, opts);
+        }
       }
     }
     // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
       if (base + k < n) {
-        if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
-        compute(d[k], tb[k % 2], opts);
+        const int kn = k + 1 < NS - 1 ? k + 1 : k;  // (the last one reloads its own table)
+        if constexpr (STAGED) {
+          compute(d[k], tb[0], d[kn].loc, opts);
+        } else {
+          if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
+          compute(d[k], tb[k % 2], d[k].loc, opts);
+        }
       }
     }
   };
