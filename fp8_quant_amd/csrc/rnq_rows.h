@@ -51,8 +51,10 @@ constexpr int RT = 64 * RW;
 #ifndef RNQ_ROWS_STAGES
 #define RNQ_ROWS_STAGES 2
 #endif
-constexpr int NS = RNQ_ROWS_STAGES;  // passes of input in flight per wave, plus the one in use
-static_assert(NS >= 2 && NS % 2 == 0, "the table ring alternates between two buffers");
+// passes of input in flight per wave plus the one in use, for aligned rope
+// passes (table rows through LDS); other modes use two
+constexpr int NS_STAGED = RNQ_ROWS_STAGES;
+static_assert(NS_STAGED >= 2, "at least the pass in use and the next one");
 
 // Variants of the pass loop chosen once per wave: GEN = per-pass branches for
 // fp8_max below 1 or a clamp that can bind; FULL = the rope tail is the whole row.
@@ -327,6 +329,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     if constexpr (STAGED) load_table(t, next);
   };
 
+  constexpr int NS = STAGED ? NS_STAGED : 2;  // (two: the register table ring alternates)
   // ---- software pipeline over this wave's n passes: input NS - 1 passes
   // ahead, table values one pass ahead (ring slots are compile-time indices).
   // The first loads go out before the weights are staged.
