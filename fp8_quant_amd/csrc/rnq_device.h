@@ -118,6 +118,10 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16_nt(rsrc_t r, uint32_t off, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, kNonTemporal);
+}
 __device__ __forceinline__ void buf_store8_nt(rsrc_t r, uint32_t off, uint2 v) {
   const u32x2 w = {v.x, v.y};
   __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);

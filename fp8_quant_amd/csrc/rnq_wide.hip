@@ -93,133 +93,175 @@ __global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
   }
 }
 
-// Backward. BT threads; thread i owns chunks i, i+BT, ... (KC of them). Loads
-// of the next RING-1 rows are kept in flight ahead of the row being computed.
-template <class DT, int KC, int BT>
+// Backward. BT threads; thread i owns chunks i, i+BT, ... (KC of them). The
+// workgroup walks its rows in batches of RB: one barrier per batch for each of
+// the two row reductions (sum of squares when rstd is recomputed, then
+// mean(g * xn)), and the next batch's loads are in flight while a batch is
+// computed. Every global access is a buffer access with a row-uniform
+// descriptor; lanes past the row's end use offsets outside the descriptor's
+// range (dropped by the hardware), and a batch that runs past the workgroup's
+// last row re-reads that row and writes its identical grad_x again, so no
+// access in the loop is conditional and the in-order memory counter is waited
+// on precisely. grad_w partials accumulate in ascending row order.
+template <class DT, int KC, int BT, int RB>
 __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   constexpr int BW = BT / 64;
-  __shared__ double part_d[2][BW];
-  __shared__ float part_f[2][BW];
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  __shared__ double part_d[2][RB][BW];
+  __shared__ float part_f[2][RB][BW];
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = tid >> 6;
   const uint32_t nch = p.N / 8;
   const uint32_t r0 = blockIdx.x * p.rows_per_block;
-  const uint32_t r1 = min(r0 + p.rows_per_block, p.M);
+  const uint32_t r1 = min(r0 + p.rows_per_block, p.M);  // r0 < r1: the partition gives every block rows
+  const uint32_t row_bytes = 2u * p.N;
+  if (r0 >= r1) return;  // (not reached with bwd_partition's blocks)
 
-  float w[KC][8], dw[KC][8];
+  extern __shared__ uint4 w_s[];  // the weight row (16-bit values, N * 2 bytes), read where it is used
+  float dw[KC][8];
   bool ok[KC];
+  uint32_t off[KC];  // byte offset of the lane's chunk k in a row (out of range past the end)
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     const uint32_t c = tid + BT * k;
     ok[k] = c < nch;
-    if (ok[k]) unpack8<DT>(*(const uint4*)(p.w + 8 * (size_t)c), w[k]);
-    else for (int i = 0; i < 8; ++i) w[k][i] = 0.f;
+    off[k] = ok[k] ? 16u * c : kOutOfRange;
+    const uint4 wc = buf_load16(make_rsrc(p.w, row_bytes), off[k]);
+    if (ok[k]) w_s[c] = wc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dw[k][i] = 0.f;
   }
+  auto wk = [&](int k, float* wf) {  // this lane's 8 weights of chunk k (zeros past the row's end)
+    const uint4 wc = w_s[ok[k] ? tid + BT * k : 0u];
+    unpack8<DT>(ok[k] ? wc : make_uint4(0, 0, 0, 0), wf);
+  };
+  __syncthreads();
 
-  auto load_row = [&](uint32_t row, uint4* xs, uint4* gs) {
+  auto load_batch = [&](uint32_t first, uint4 (&xs)[RB][KC], uint4 (&gs)[RB][KC]) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      xs[k] = make_uint4(0, 0, 0, 0);
-      gs[k] = make_uint4(0, 0, 0, 0);
-      if (row < r1 && ok[k]) {
-        const size_t off = (size_t)row * p.N + 8 * (size_t)(tid + BT * k);
-        xs[k] = load_stream16(p.x + off);
-        gs[k] = load_stream16(p.gy + off);
+    for (int j = 0; j < RB; ++j) {
+      const size_t row = min(first + (uint32_t)j, r1 - 1);
+      const rsrc_t rx = make_rsrc(p.x + row * p.N, row_bytes);
+      const rsrc_t rg = make_rsrc(p.gy + row * p.N, row_bytes);
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        xs[j][k] = buf_load16_nt(rx, off[k]);
+        gs[j][k] = buf_load16_nt(rg, off[k]);
       }
     }
   };
 
-  constexpr int RING = KC >= 4 ? 2 : (KC == 2 ? 3 : 4);  // bounded by registers
-  uint4 xr[RING][KC], gr[RING][KC];
-#pragma unroll
-  for (int j = 0; j < RING - 1; ++j) load_row(r0 + j, xr[j], gr[j]);
-
+  uint4 xr[2][RB][KC], gr[2][RB][KC];
+  load_batch(r0, xr[0], gr[0]);
   uint32_t parity = 0;
-  for (uint32_t row = r0; row < r1; ++row) {
-    load_row(row + RING - 1, xr[RING - 1], gr[RING - 1]);
-    uint4 (&x0)[KC] = xr[0];
-    uint4 (&g0)[KC] = gr[0];
 
-    float xf[KC][8], gf[KC][8];
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      unpack8<DT>(x0[k], xf[k]);
-      unpack8<DT>(g0[k], gf[k]);
-    }
-
-    float rstd;
+  // one batch; cur / nxt are compile-time ring slots
+  auto batch = [&](uint32_t first, uint4 (&xc)[RB][KC], uint4 (&gc)[RB][KC], uint4 (&xn_)[RB][KC],
+                   uint4 (&gn)[RB][KC]) {
+    load_batch(first + RB, xn_, gn);
+    float rstd[RB];
     if (p.rstd != nullptr) {
-      rstd = p.rstd[row];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) rstd[j] = p.rstd[min(first + (uint32_t)j, r1 - 1)];
     } else {
-      double acc = 0.0;
 #pragma unroll
-      for (int k = 0; k < KC; ++k)
+      for (int j = 0; j < RB; ++j) {
+        double acc = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)xf[k][i], (double)xf[k][i], acc);
-      acc = group_sum<64>(acc);
-      if ((tid & 63) == 0) part_d[parity][wave] = acc;
+        for (int k = 0; k < KC; ++k) {
+          float xf[8];
+          unpack8<DT>(xc[j][k], xf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)xf[i], (double)xf[i], acc);
+        }
+        acc = group_sum<64>(acc);
+        if ((tid & 63) == 0) part_d[parity][j][wave] = acc;
+      }
       __syncthreads();
-      double tot = part_d[parity][0];
 #pragma unroll
-      for (int v = 1; v < BW; ++v) tot += part_d[parity][v];
-      rstd = rstd_of((float)tot / (float)p.N + p.eps);
+      for (int j = 0; j < RB; ++j) {
+        double tot = part_d[parity][j][0];
+#pragma unroll
+        for (int v = 1; v < BW; ++v) tot += part_d[parity][j][v];
+        rstd[j] = rstd_of((float)tot / (float)p.N + p.eps);
+      }
     }
 
     // C = mean(g * xn): lane-sequential fp32 sum, wave butterfly, waves in ascending order
-    float xn[KC][8], g[KC][8];
-    float dot = 0.f;
+    float C[RB];
 #pragma unroll
-    for (int k = 0; k < KC; ++k)
+    for (int j = 0; j < RB; ++j) {
+      float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xn[k][i] = xf[k][i] * rstd;
-        g[k][i] = gf[k][i] * w[k][i];
-        dot += g[k][i] * xn[k][i];
+      for (int k = 0; k < KC; ++k) {
+        float xf[8], gf[8], w[8];
+        unpack8<DT>(xc[j][k], xf);
+        unpack8<DT>(gc[j][k], gf);
+        wk(k, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot += (gf[i] * w[i]) * (xf[i] * rstd[j]);
       }
-    dot = group_sum<64>(dot);
-    if ((tid & 63) == 0) part_f[parity][wave] = dot;
+      dot = group_sum<64>(dot);
+      if ((tid & 63) == 0) part_f[parity][j][wave] = dot;
+    }
     __syncthreads();
-    float tot = part_f[parity][0];
 #pragma unroll
-    for (int v = 1; v < BW; ++v) tot += part_f[parity][v];
+    for (int j = 0; j < RB; ++j) {
+      float tot = part_f[parity][j][0];
+#pragma unroll
+      for (int v = 1; v < BW; ++v) tot += part_f[parity][j][v];
+      C[j] = tot / (float)p.N;
+    }
     parity ^= 1u;
-    const float C = tot / (float)p.N;
 
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      if (!ok[k]) continue;
-      float o[8];
+    for (int j = 0; j < RB; ++j) {
+      const uint32_t row = min(first + (uint32_t)j, r1 - 1);
+      const bool real = first + (uint32_t)j < r1;  // a repeated row adds nothing to grad_w
+      const rsrc_t rdx = make_rsrc(p.gx + (size_t)row * p.N, row_bytes);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o[i] = rstd * (g[k][i] - xn[k][i] * C);
-        dw[k][i] += gf[k][i] * xn[k][i];
+      for (int k = 0; k < KC; ++k) {
+        float xf[8], gf[8], o[8], w[8];
+        unpack8<DT>(xc[j][k], xf);
+        unpack8<DT>(gc[j][k], gf);
+        wk(k, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xn = xf[i] * rstd[j];
+          o[i] = rstd[j] * ((gf[i] * w[i]) - xn * C[j]);
+          if (real) dw[k][i] += gf[i] * xn;
+        }
+        buf_store16_nt(rdx, off[k], pack8<DT>(o));
       }
-      const uint4 v = pack8<DT>(o);
-      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)(p.gx + (size_t)row * p.N + 8 * (size_t)(tid + BT * k)));
     }
-#pragma unroll
-    for (int j = 0; j < RING - 1; ++j)
-#pragma unroll
-      for (int k = 0; k < KC; ++k) { xr[j][k] = xr[j + 1][k]; gr[j][k] = gr[j + 1][k]; }
+  };
+
+  // batches alternate between the two ring slots
+  const uint32_t nb = (r1 - r0 + RB - 1) / RB;
+  uint32_t b = 0;
+  for (; b + 2 <= nb; b += 2) {
+    batch(r0 + b * RB, xr[0], gr[0], xr[1], gr[1]);
+    batch(r0 + (b + 1) * RB, xr[1], gr[1], xr[0], gr[0]);
   }
+  if (b < nb) batch(r0 + b * RB, xr[0], gr[0], xr[1], gr[1]);
 
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    if (!ok[k]) continue;
-    float* dst = p.partial + (size_t)blockIdx.x * p.N + 8 * (size_t)(tid + BT * k);
-    *(float4*)dst = make_float4(dw[k][0], dw[k][1], dw[k][2], dw[k][3]);
-    *(float4*)(dst + 4) = make_float4(dw[k][4], dw[k][5], dw[k][6], dw[k][7]);
+    const rsrc_t rp = make_rsrc(p.partial + (size_t)blockIdx.x * p.N, 4u * p.N);
+    const uint32_t po = ok[k] ? 2u * off[k] : kOutOfRange;  // 8 floats per chunk
+    buf_store16(rp, po, make_uint4(__float_as_uint(dw[k][0]), __float_as_uint(dw[k][1]),
+                                   __float_as_uint(dw[k][2]), __float_as_uint(dw[k][3])));
+    buf_store16(rp, po + 16u, make_uint4(__float_as_uint(dw[k][4]), __float_as_uint(dw[k][5]),
+                                         __float_as_uint(dw[k][6]), __float_as_uint(dw[k][7])));
   }
 }
 
-// grad_w[j] = sum over b of partial[b, j] in a fixed order. A workgroup owns 64
-// columns (16 float4 column groups); its 16 row phases each add partial rows
-// phase, phase+16, ... in ascending order, then phase sums are added in
-// ascending phase order.
-constexpr int RQ = 16;  // column float4 groups per workgroup
-constexpr int RP = 16;  // row phases
+// grad_w[j] = sum over b of partial[b, j] in a fixed order. A workgroup owns
+// RQ float4 column groups; its RP row phases each add partial rows phase,
+// phase + RP, ... in ascending order, then the phase sums are added in
+// ascending phase order. RQ = 4 gives N / 16 workgroups (256 at N = 4096).
+constexpr int RQ = 4;   // column float4 groups per workgroup
+constexpr int RP = 64;  // row phases
 __global__ __launch_bounds__(RQ * RP) void dw_reduce_kernel(const float* __restrict__ partial, float* __restrict__ gw,
                                                            uint32_t blocks, uint32_t N) {
   __shared__ float4 acc_s[RP][RQ];
@@ -237,7 +279,6 @@ __global__ __launch_bounds__(RQ * RP) void dw_reduce_kernel(const float* __restr
   __syncthreads();
   if (ph == 0 && ok) {
     float4 t = acc_s[0][cq];
-#pragma unroll
     for (int i = 1; i < RP; ++i) {
       const float4 v = acc_s[i][cq];
       t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
@@ -260,17 +301,23 @@ static hipError_t fwd_kc(const WideFwdParams& p, int kc, dim3 g, dim3 b, hipStre
   return hipGetLastError();
 }
 
-// 512 threads for rows wider than 2048 (1, 2 or 4 chunks per lane), 256 below (1 chunk).
+// 512 threads for rows wider than 2048 (1, 2 or 4 chunks per lane), 256 below
+// (1 chunk); rows per batch: 4 chunks' worth of rows per lane.
+#ifndef RNQ_BWD_BATCH
+#define RNQ_BWD_BATCH 2
+#endif
 template <class DT>
 static hipError_t bwd_kc(const WideBwdParams& p, int kc, dim3 g, hipStream_t s) {
+  constexpr int B = RNQ_BWD_BATCH;
+  const size_t lds = 2 * (size_t)p.N;  // the weight row
   if (p.N <= 2048) {
-    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256>), g, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B>), g, dim3(256), lds, s, p);
     return hipGetLastError();
   }
   switch (kc) {
-    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512>), g, dim3(512), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512>), g, dim3(512), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512>), g, dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512, B>), g, dim3(512), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512, (B > 2 ? B / 2 : 1)>), g, dim3(512), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512, (B > 4 ? B / 4 : 1)>), g, dim3(512), lds, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -291,10 +338,15 @@ hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream
   return bf16 ? fwd_kc<BF16>(p, kc, grid, block, stream) : fwd_kc<F16>(p, kc, grid, block, stream);
 }
 
+// Blocks of contiguous rows, every block owning at least one row: about 512
+// (two workgroups per CU) up to 8192 rows, 256 above (fewer partial rows of
+// grad_w to write and read back).
 uint32_t bwd_blocks(int64_t M, int64_t N) {
   (void)N;
-  const int64_t target = 256;
-  return (uint32_t)(M < target ? (M > 0 ? M : 1) : target);
+  if (M <= 0) return 1;
+  const int64_t target = M <= 8192 ? 512 : 256;
+  const int64_t rpb = (M + target - 1) / target;
+  return (uint32_t)((M + rpb - 1) / rpb);
 }
 
 hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream) {
