@@ -80,7 +80,10 @@ int rnq_abi_version(void);
 rnq_status rnq_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out,
                            int64_t M, int64_t N, float eps, int dtype, void* stream);
 
-/* Bytes of device workspace rnq_rmsnorm_bwd needs for an [M,N] problem. */
+/* Bytes of device workspace rnq_rmsnorm_bwd needs for an [M,N] problem:
+ * P * N * 4, where the rows are split into P contiguous blocks,
+ * P = ceil(M / ceil(M / T)) with T = 512 for M <= 8192 and 256 above
+ * (0 when M or N is 0). */
 size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /*
@@ -91,8 +94,8 @@ size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
  *                                                      w's dtype afterwards; the caller may)
  * rstd [M] fp32 may be NULL, in which case it is recomputed from x as in the
  * forward. grad_w is reduced deterministically: per-block partial sums over a
- * fixed row partition are written to `workspace`, then summed in ascending
- * block order; results are bitwise reproducible for a given (M, N).
+ * fixed row partition are written to `workspace`, then summed per column in
+ * a fixed order; results are bitwise reproducible for a given (M, N).
  * workspace_bytes must be >= rnq_rmsnorm_bwd_workspace_size(M, N); the
  * workspace is scratch owned by the caller (16-byte aligned).
  */

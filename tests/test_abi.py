@@ -93,7 +93,9 @@ def test_rmsnorm_argument_validation():
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 128, 64, 1, 1e-6, 0, None) == 1
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 3
     need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 4096)
-    assert need == 256 * 4096 * 4
+    assert need == 512 * 4096 * 4  # 512 blocks of 8 rows
+    assert lib.rnq_rmsnorm_bwd_workspace_size(16384, 4096) == 256 * 4096 * 4
+    assert lib.rnq_rmsnorm_bwd_workspace_size(257, 1024) == 257 * 1024 * 4  # one row per block
     assert lib.rnq_rmsnorm_bwd_workspace_size(0, 4096) == 0
     assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, 4096, 4096, 1e-6, 0, None) == 5
     assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, need, 4096, 4096, 1e-6, 0, None) == 5
