@@ -6,12 +6,10 @@
 //   xn = x * rstd, g = grad_y * w,
 //   grad_x = rstd * (g - xn * mean(g * xn)),  grad_w = sum over rows of grad_y * xn.
 //
-// Mapping: one 256-thread workgroup (4 waves) per row at a time; thread i owns
-// 16-byte chunks i, i+256, ... of the row (KC chunks). Row sums: per-lane
-// partials, a DPP/shuffle butterfly over the wave, then the four wave totals
-// are added in ascending wave order through LDS (double-buffered by row
-// parity so one barrier per reduction suffices). The next row's loads are
-// issued before the current row is reduced.
+// Mapping: a workgroup (256 threads, or 512 for the backward of wide rows)
+// holds whole rows; thread i owns 16-byte chunks i, i+256, ... of a row (KC
+// chunks). Row sums: per-lane partials, a DPP/shuffle butterfly over the
+// wave, then the wave totals are added in ascending wave order through LDS.
 //
 // Backward grad_w is deterministic: workgroup b owns a fixed contiguous range
 // of rows and accumulates grad_y * xn for its columns in registers, in row
@@ -25,71 +23,75 @@ namespace rnq {
 constexpr int WT = 256;  // threads per workgroup
 constexpr int WW = WT / 64;
 
-template <class DT, int KC>
+// Forward. Workgroup b normalises rows b*RB .. b*RB + RB - 1 (a last partial
+// group repeats row M - 1, writing identical bytes). All its loads are issued
+// at once (buffer accesses, lanes past the row's end out of the descriptor's
+// range); one barrier for the RB rows' sums of squares.
+template <class DT, int KC, int RB>
 __global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
-  __shared__ double part[2][WW];
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  __shared__ double part[RB][WW];
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = tid >> 6;
   const uint32_t nch = p.N / 8;
-  uint32_t row = blockIdx.x;
-  if (row >= p.M) return;
+  const uint32_t row_bytes = 2u * p.N;
+  const uint32_t first = blockIdx.x * RB;
 
-  float w[KC][8];
+  uint32_t off[KC];
   bool ok[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     const uint32_t c = tid + WT * k;
     ok[k] = c < nch;
-    if (ok[k]) unpack8<DT>(*(const uint4*)(p.w + 8 * (size_t)c), w[k]);
-    else for (int i = 0; i < 8; ++i) w[k][i] = 0.f;
+    off[k] = ok[k] ? 16u * c : kOutOfRange;
   }
-
-  uint4 x[KC];
+  uint4 x[RB][KC];
 #pragma unroll
-  for (int k = 0; k < KC; ++k)
-    x[k] = ok[k] ? *(const uint4*)(p.x + (size_t)row * p.N + 8 * (size_t)(tid + WT * k)) : make_uint4(0, 0, 0, 0);
-
-  uint32_t parity = 0;
-  for (; row < p.M; row += gridDim.x) {
-    const uint32_t nrow = row + gridDim.x;
-    const bool has_next = nrow < p.M;
-    uint4 nx[KC];
+  for (int j = 0; j < RB; ++j) {
+    const rsrc_t rx = make_rsrc(p.x + (size_t)min(first + (uint32_t)j, p.M - 1) * p.N, row_bytes);
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      nx[k] = x[k];
-      if (has_next && ok[k]) nx[k] = *(const uint4*)(p.x + (size_t)nrow * p.N + 8 * (size_t)(tid + WT * k));
-    }
+    for (int k = 0; k < KC; ++k) x[j][k] = buf_load16_nt(rx, off[k]);
+  }
+  uint4 wr[KC];
+  const rsrc_t rw = make_rsrc(p.w, row_bytes);
+#pragma unroll
+  for (int k = 0; k < KC; ++k) wr[k] = buf_load16(rw, off[k]);
 
-    float xf[KC][8];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      unpack8<DT>(x[k], xf[k]);
+      float xf[8];
+      unpack8<DT>(x[j][k], xf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)xf[k][i], (double)xf[k][i], acc);
+      for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)xf[i], (double)xf[i], acc);
     }
     acc = group_sum<64>(acc);
-    if ((tid & 63) == 0) part[parity][wave] = acc;
-    __syncthreads();
-    double tot = part[parity][0];
-#pragma unroll
-    for (int v = 1; v < WW; ++v) tot += part[parity][v];
-    parity ^= 1u;
+    if ((tid & 63) == 0) part[j][wave] = acc;
+  }
+  __syncthreads();
 
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    double tot = part[j][0];
+#pragma unroll
+    for (int v = 1; v < WW; ++v) tot += part[j][v];
     const float ssq = (float)tot;
     const float ms = ssq / (float)p.N;
     const float rstd = rstd_of(ms + p.eps);
+    const uint32_t row = min(first + (uint32_t)j, p.M - 1);
+    const rsrc_t ry = make_rsrc(p.y + (size_t)row * p.N, row_bytes);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      if (!ok[k]) continue;
-      float o[8];
+      float xf[8], w[8], o[8];
+      unpack8<DT>(x[j][k], xf);
+      unpack8<DT>(wr[k], w);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = (xf[k][i] * rstd) * w[k][i];
-      *(uint4*)(p.y + (size_t)row * p.N + 8 * (size_t)(tid + WT * k)) = pack8<DT>(o);
+      for (int i = 0; i < 8; ++i) o[i] = (xf[i] * rstd) * w[i];
+      buf_store16_nt(ry, off[k], pack8<DT>(o));
     }
     if (p.rstd != nullptr && tid == 0) p.rstd[row] = rstd;
-#pragma unroll
-    for (int k = 0; k < KC; ++k) x[k] = nx[k];
   }
 }
 
@@ -289,13 +291,18 @@ __global__ __launch_bounds__(RQ * RP) void dw_reduce_kernel(const float* __restr
 
 // ----------------------------------------------------------------- launchers
 
+#ifndef RNQ_FWD_ROWS
+#define RNQ_FWD_ROWS 1
+#endif
 template <class DT>
-static hipError_t fwd_kc(const WideFwdParams& p, int kc, dim3 g, dim3 b, hipStream_t s) {
+static hipError_t fwd_kc(const WideFwdParams& p, int kc, hipStream_t s) {
+  constexpr int B = RNQ_FWD_ROWS;
+  const dim3 b(WT);
   switch (kc) {
-    case 1: hipLaunchKernelGGL((wide_fwd_kernel<DT, 1>), g, b, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((wide_fwd_kernel<DT, 2>), g, b, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((wide_fwd_kernel<DT, 4>), g, b, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((wide_fwd_kernel<DT, 8>), g, b, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((wide_fwd_kernel<DT, 1, B>), dim3((p.M + B - 1) / B), b, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((wide_fwd_kernel<DT, 2, B>), dim3((p.M + B - 1) / B), b, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((wide_fwd_kernel<DT, 4, 1>), dim3(p.M), b, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((wide_fwd_kernel<DT, 8, 1>), dim3(p.M), b, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -332,10 +339,7 @@ static int chunks_per_lane(uint32_t N, uint32_t threads) {
 
 hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream) {
   const int kc = chunks_per_lane(p.N, WT);
-  uint32_t blocks = 2048;  // 8 workgroups per CU; each walks rows with a grid stride
-  if (blocks > p.M) blocks = p.M;
-  dim3 grid(blocks), block(WT);
-  return bf16 ? fwd_kc<BF16>(p, kc, grid, block, stream) : fwd_kc<F16>(p, kc, grid, block, stream);
+  return bf16 ? fwd_kc<BF16>(p, kc, stream) : fwd_kc<F16>(p, kc, stream);
 }
 
 // Blocks of contiguous rows, every block owning at least one row: about 512
