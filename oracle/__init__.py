@@ -43,6 +43,8 @@ from .prologue import (
     norm_rope_quant_rows,
     qk_norm_rope_fp8,
     rmsnorm_rope,
+    quantize_groups,
+    rmsnorm_rope_fp8_grouped,
     truth_norm_rope,
 )
 from .backward import rmsnorm_bwd
@@ -52,4 +54,5 @@ __all__ = [
     "E4M3_TABLE", "dtype_round", "dtype_to_f32", "sum_squares_f32", "sum_squares_exact_mask",
     "rmsnorm_fwd", "rope_tail", "quantize_rows", "norm_rope_quant_rows", "qk_norm_rope_fp8",
     "rmsnorm_rope", "truth_norm_rope", "rmsnorm_bwd",
+    "quantize_groups", "rmsnorm_rope_fp8_grouped",
 ]

@@ -36,6 +36,8 @@ __all__ = [
     "norm_rope_quant_rows",
     "qk_norm_rope_fp8",
     "rmsnorm_rope",
+    "quantize_groups",
+    "rmsnorm_rope_fp8_grouped",
     "truth_norm_rope",
 ]
 
@@ -155,6 +157,33 @@ def rmsnorm_rope(x_bits, w_bits, cos, sin, eps=1e-6, dtype="bf16", rows_per_toke
     y, _, _ = norm_rope_quant_rows(x_bits, w_bits, np.asarray(cos)[t], np.asarray(sin)[t],
                                    eps, 448.0, dtype, quant=False)
     return y
+
+
+def quantize_groups(y_bits: np.ndarray, group_size: int, fp8_max: float, dtype: str = "bf16"):
+    """Per-group absmax FP8 (chapter 13 fusion page, ``rms_norm_rope_quant_fused``:
+    every ``group_size`` consecutive elements of a row share one scale, the
+    group's absmax clamped below at 1e-4 over fp8_max; y / scale clamped to
+    +-fp8_max, then cast). Returns (codes [M, N] uint8, scale [M, N / group_size] float32).
+    """
+    y = dtype_to_f32(y_bits, dtype)
+    M, N = y.shape
+    if N % group_size:
+        raise ValueError("group_size must divide the row")
+    groups = y.reshape(M, N // group_size, group_size)
+    amax = np.abs(groups).max(axis=-1)
+    scale = np.maximum(amax, F32(1e-4)) / F32(fp8_max)
+    q = groups / scale[:, :, None]
+    q = np.minimum(np.maximum(q, -F32(fp8_max)), F32(fp8_max))
+    return e4m3_encode(q).reshape(M, N), scale.astype(F32)
+
+
+def rmsnorm_rope_fp8_grouped(x_bits, w_bits, cos, sin, group_size, eps=1e-6, fp8_max=448.0, dtype="bf16",
+                             rows_per_token=1, rows=None):
+    """RMSNorm -> partial RoPE -> per-group FP8 over rows of any width (row r uses
+    table row r // rows_per_token). Returns (y_bits, codes, scale [M, N / group_size])."""
+    y = rmsnorm_rope(x_bits, w_bits, cos, sin, eps, dtype, rows_per_token, rows)
+    codes, scale = quantize_groups(y, group_size, fp8_max, dtype)
+    return y, codes, scale
 
 
 def truth_norm_rope(x_bits, w_bits, cos_rows, sin_rows, eps, dtype="bf16", round_intermediates=False):

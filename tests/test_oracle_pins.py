@@ -335,3 +335,67 @@ def test_agrees_with_torch_reference_up_to_summation_order():
     d = np.abs(ours.astype(np.int32) - yb.astype(np.int32))
     assert np.all(d <= 1)
     assert np.mean(d == 0) > 0.9995
+
+
+# ----------------------------------------------------------------- per-group scales
+
+
+def test_one_group_per_row_equals_the_per_row_scale():
+    y = _rows(64, 256, 70)
+    codes_g, scale_g = oracle.quantize_groups(y, 256, 448.0)
+    codes_r, scale_r = oracle.quantize_rows(y, 448.0)
+    assert np.array_equal(codes_g, codes_r)
+    assert np.array_equal(scale_g[:, 0].view(np.uint32), scale_r.view(np.uint32))
+
+
+@pytest.mark.parametrize("group_size", [16, 64, 128])
+def test_each_group_scale_is_its_own_absmax_over_fp8_max(group_size):
+    rng = np.random.default_rng(71 + group_size)
+    M, N = 8, 512
+    G = N // group_size
+    # every group gets its own magnitude, so a group read along the wrong axis shows
+    mags = 2.0 ** rng.integers(-20, 6, size=(M, G))
+    vals = rng.standard_normal((M, N)) * np.repeat(mags, group_size, axis=1)
+    vals[0, :group_size] = 0.0  # one group entirely zero: the 1e-4 floor
+    y = _bf16(vals.astype(np.float32))
+    codes, scale = oracle.quantize_groups(y, group_size, 448.0)
+    yv = codecs.bf16_to_f32(y)
+    for i in range(M):
+        for g in range(G):
+            elems = [abs(float(v)) for v in yv[i, g * group_size:(g + 1) * group_size]]
+            a = max(max(elems), float(np.float32(1e-4)))
+            assert scale[i, g].tobytes() == _exact_div_f32(a, 448.0).tobytes()
+            mag = codes[i, g * group_size:(g + 1) * group_size] & 0x7F
+            if max(elems) >= 1e-4:
+                assert mag.max() == 0x7E
+            else:  # below the floor: the largest code is that of amax / scale, no longer 448
+                q = _exact_div_f32(max(elems), float(scale[i, g]))
+                assert mag.max() == (codecs.e4m3_encode(np.float32(q)) & 0x7F)
+    assert np.all(codes[0, :group_size] & 0x7F == 0)
+
+
+def test_groups_are_independent():
+    y = _rows(16, 512, 72)
+    codes, scale = oracle.quantize_groups(y, 128, 448.0)
+    y2 = y.copy()
+    y2[:, 128:256] = _bf16(codecs.bf16_to_f32(y[:, 128:256]) * 37.0)
+    codes2, scale2 = oracle.quantize_groups(y2, 128, 448.0)
+    keep = np.r_[0:128, 256:512]
+    assert np.array_equal(codes[:, keep], codes2[:, keep])
+    assert np.array_equal(scale[:, [0, 2, 3]], scale2[:, [0, 2, 3]])
+    assert not np.array_equal(scale[:, 1], scale2[:, 1])
+
+
+def test_grouped_pipeline_decodes_within_e4m3_rounding():
+    x = _rows(32, 1024, 73)
+    w = _bf16(1 + 0.1 * np.random.default_rng(74).standard_normal(1024))
+    c, s = _table(32, 64, 75)
+    y, codes, scale = oracle.rmsnorm_rope_fp8_grouped(x, w, c, s, 128)
+    assert np.array_equal(y, oracle.rmsnorm_rope(x, w, c, s))
+    yv = codecs.bf16_to_f32(y).astype(np.float64)
+    sc = np.repeat(scale.astype(np.float64), 128, axis=1)
+    dec = codecs.e4m3_decode(codes).astype(np.float64) * sc
+    err = np.abs(dec - yv)
+    normal = np.abs(yv) / sc >= 2.0**-6
+    assert np.all(err[normal] <= 2.0**-4 * np.abs(yv[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0**-10 * sc[~normal] * (1 + 1e-6))
