@@ -135,6 +135,28 @@ def bench_norm_rope(torch, rnq, workloads, ledger, name, steps, warmup):
     return {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
 
 
+def bench_grouped(torch, rnq, workloads, ledger, name, steps, warmup):
+    wl = workloads.WORKLOADS[name]
+    d = workloads.generate(name)
+    M, N, R, G = d["rows"], d["width"], d["rope_dim"], d["group_size"]
+    led = ledger.grouped_bytes(M, N, R, G, d["rows_per_token"], write_y=wl.write_y)
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(led["total"])
+    sets = [{"x": d["x"].to(dev), "cos": d["cos"].to(dev), "sin": d["sin"].to(dev),
+             "codes": torch.empty((M, N), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((M, N // G), dtype=torch.float32, device=dev),
+             "y": torch.empty_like(d["x"], device=dev) if wl.write_y else None} for _ in range(n_sets)]
+    w = d["w"].to(dev)
+
+    launches = [rnq.prepare_rmsnorm_rope_fp8_grouped(s["x"], w, s["cos"], s["sin"], s["codes"], s["scales"], s["y"],
+                                                     group_size=G, rows_per_token=d["rows_per_token"],
+                                                     eps=wl.eps, fp8_max=wl.fp8_max) for s in sets]
+    ms = _timed(torch, launches, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
+
+
 def bench_rmsnorm(torch, rnq, workloads, ledger, name, steps, warmup):
     d = workloads.generate(name)
     M, N = d["rows"], d["width"]
@@ -297,6 +319,7 @@ def main() -> int:
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_small", steps, warm)))
         paths += [_summary(r) for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, warm)]
         paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
+        paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 20)))
         out["other_paths"] = paths
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)

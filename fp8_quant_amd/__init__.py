@@ -8,8 +8,8 @@ computation runs in the HIP kernels; there is no CPU path. If the library has
 not been built, the first call raises.
 
 Convenience wrappers (``qk_norm_rope_fp8``, ``rmsnorm``, ``rmsnorm_bwd``,
-``rmsnorm_rope``) allocate the outputs with torch and call the same entry
-points.
+``rmsnorm_rope``, ``rmsnorm_rope_fp8_grouped``) allocate the outputs with torch
+and call the same entry points.
 """
 
 from __future__ import annotations
@@ -28,7 +28,9 @@ __all__ = [
     "rnq_rmsnorm_fwd",
     "rnq_rmsnorm_bwd",
     "rnq_rmsnorm_bwd_workspace_size",
+    "rnq_rmsnorm_rope_fp8_grouped",
     "prepare_qk_norm_rope_fp8",
+    "prepare_rmsnorm_rope_fp8_grouped",
     "prepare_rmsnorm_rope",
     "prepare_rmsnorm_fwd",
     "prepare_rmsnorm_bwd",
@@ -36,6 +38,7 @@ __all__ = [
     "rmsnorm",
     "rmsnorm_bwd",
     "rmsnorm_rope",
+    "rmsnorm_rope_fp8_grouped",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -49,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "rnq_rmsnorm_bwd",
     "rnq_rmsnorm_rope",
     "rnq_qk_norm_rope_fp8",
+    "rnq_rmsnorm_rope_fp8_grouped",
 )
 
 RNQ_BF16 = 0
@@ -96,6 +100,8 @@ def load_library():
     lib.rnq_rmsnorm_rope.restype = i32
     lib.rnq_qk_norm_rope_fp8.argtypes = [vp] * 12 + [i64] * 5 + [f32, f32, i32, vp]
     lib.rnq_qk_norm_rope_fp8.restype = i32
+    lib.rnq_rmsnorm_rope_fp8_grouped.argtypes = [vp] * 7 + [i64] * 5 + [f32, f32, i32, vp]
+    lib.rnq_rmsnorm_rope_fp8_grouped.restype = i32
     _lib = lib
     return lib
 
@@ -271,6 +277,34 @@ def prepare_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, e
     return _launcher(lib.rnq_rmsnorm_bwd, args)
 
 
+def rnq_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, group_size: int = 128,
+                                 rows_per_token: int = 1, eps: float = 1e-6, fp8_max: float = 448.0,
+                                 stream=None) -> None:
+    """RMSNorm + RoPE + FP8 with one scale per group into caller-provided outputs."""
+    prepare_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y, group_size=group_size,
+                                     rows_per_token=rows_per_token, eps=eps, fp8_max=fp8_max, stream=stream)()
+
+
+def prepare_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, group_size: int = 128,
+                                     rows_per_token: int = 1, eps: float = 1e-6, fp8_max: float = 448.0,
+                                     stream=None):
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    half = 0 if cos is None else cos.shape[-1]
+    _expect(w, x.dtype, (N,), "w")
+    _expect(y, x.dtype, (M, N), "y")
+    if cos is not None:
+        _expect(cos, torch.float32, (M // max(rows_per_token, 1), half), "cos")
+        _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
+    if codes.dtype not in (torch.uint8, torch.float8_e4m3fn) or tuple(codes.shape) != (M, N):
+        raise ValueError(f"codes: expected uint8 or float8_e4m3fn of shape {(M, N)}")
+    _expect(scales, torch.float32, (M, N // group_size if group_size > 0 else 0), "scales")
+    args = (_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), _ptr(codes), _ptr(scales), M, N, 2 * half,
+            rows_per_token, group_size, eps, fp8_max, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_rope_fp8_grouped, args)
+
+
 # ------------------------------------------------------- allocating wrappers
 
 
@@ -316,3 +350,17 @@ def rmsnorm_rope(x, w, cos, sin, *, rows_per_token=1, eps=1e-6):
     y = torch.empty_like(x)
     rnq_rmsnorm_rope(x, w, cos, sin, y, rows_per_token=rows_per_token, eps=eps)
     return y
+
+
+def rmsnorm_rope_fp8_grouped(x, w, cos, sin, *, group_size=128, rows_per_token=1, eps=1e-6, fp8_max=448.0,
+                             return_y=False):
+    """Returns (codes as torch.float8_e4m3fn [M, N], scales [M, N / group_size][, y])."""
+    torch = _torch()
+    M, N = x.shape
+    codes = torch.empty((M, N), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, N // group_size), dtype=torch.float32, device=x.device)
+    y = torch.empty_like(x) if return_y else None
+    rnq_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y, group_size=group_size,
+                                 rows_per_token=rows_per_token, eps=eps, fp8_max=fp8_max)
+    out = (codes.view(torch.float8_e4m3fn), scales)
+    return out + (y,) if return_y else out

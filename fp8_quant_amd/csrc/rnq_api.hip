@@ -234,6 +234,53 @@ rnq_status rnq_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_ou
   return hip_status(launch_wide_fwd(p, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_fwd");
 }
 
+rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const float* cos, const float* sin,
+                                        void* y, uint8_t* codes, float* scales, int64_t M, int64_t N,
+                                        int64_t rope_dim, int64_t rows_per_token, int64_t group_size, float eps,
+                                        float fp8_max, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
+  if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
+  if (rope_dim > 1024) return fail(RNQ_ERR_UNSUPPORTED, "rope_dim must be at most 1024 (got %lld)", (long long)rope_dim);
+  if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
+  if (M % rows_per_token != 0)
+    return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
+  if (group_size <= 0 || (N > 0 && N % group_size != 0))
+    return fail(RNQ_ERR_SHAPE, "group_size must divide N (N %lld, group_size %lld)", (long long)N, (long long)group_size);
+  if (group_size < 8 || group_size > 512 || (group_size & (group_size - 1)) != 0)
+    return fail(RNQ_ERR_UNSUPPORTED, "group_size must be a power of two in [8, 512] (got %lld)", (long long)group_size);
+  if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
+  if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !codes || !scales) return fail(RNQ_ERR_NULL, "x, w, codes and scales are required");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
+  const void* a16[] = {x, w, y, cos, sin};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(codes, 8)) return fail(RNQ_ERR_UNSUPPORTED, "codes must be 8-byte aligned");
+  if (!aligned(scales, 4)) return fail(RNQ_ERR_UNSUPPORTED, "scales must be 4-byte aligned");
+
+  GroupQuantParams p = {};
+  p.x = (const uint16_t*)x;
+  p.w = (const uint16_t*)w;
+  p.cos = cos;
+  p.sin = sin;
+  p.y = (uint16_t*)y;
+  p.codes = codes;
+  p.scales = scales;
+  p.M = (uint32_t)M;
+  p.N = (uint32_t)N;
+  p.rope = (uint32_t)rope_dim;
+  p.rows_per_token = (uint32_t)rows_per_token;
+  p.group_size = (uint32_t)group_size;
+  p.eps = eps;
+  p.fp8_max = fp8_max;
+  return hip_status(launch_group_quant(p, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_rope_fp8_grouped");
+}
+
 size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
   return (size_t)bwd_blocks(M, N) * (size_t)N * sizeof(float);

@@ -1,0 +1,199 @@
+// RMSNorm -> partial NeoX RoPE -> FP8 e4m3fn with one scale per group of
+// group_size consecutive elements, over rows of up to 16384 elements.
+//
+// Operation: tilelang-tutorial chapter 13 fusion page, rms_norm_rope_quant_fused
+// (the normalised row cast to the input dtype, the tail rotated and cast, then
+// every group of group_size elements quantised with its own scale =
+// max(group absmax, 1e-4) / fp8_max, y / scale clamped to +-fp8_max and cast).
+//
+// Mapping: one 256-thread workgroup per row; thread i owns 16-byte chunks
+// i, i+256, ... (KC of them). A group of group_size elements is GL =
+// group_size / 8 consecutive chunks, i.e. GL consecutive lanes of one wave, so
+// its absmax is a DPP reduction over those lanes. The rope tail's pairs live
+// in different threads: the normalised tail goes through LDS (one barrier).
+// Every global access is a buffer access with a row-uniform descriptor (lanes
+// past the row's end use offsets outside its range).
+#include "rnq_device.h"
+#include "rnq_launch.h"
+
+namespace rnq {
+
+constexpr int GT = 256;       // threads per workgroup
+constexpr int GWV = GT / 64;  // waves
+constexpr uint32_t kMaxRope = 1024;
+
+template <class DT, int KC, int GL>
+__global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  __shared__ double part[GWV];
+  __shared__ float tail_s[kMaxRope];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t wave = tid >> 6;
+  const uint32_t row = blockIdx.x;
+  const uint32_t nch = p.N / 8;
+  const uint32_t row_bytes = 2u * p.N;
+
+  uint32_t ch[KC], off[KC];
+  bool ok[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    ch[k] = tid + GT * k;
+    ok[k] = ch[k] < nch;
+    off[k] = ok[k] ? 16u * ch[k] : kOutOfRange;
+  }
+  const rsrc_t rx = make_rsrc(p.x + (size_t)row * p.N, row_bytes);
+  const rsrc_t rw = make_rsrc(p.w, row_bytes);
+  uint4 xr[KC], wr[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    xr[k] = buf_load16_nt(rx, off[k]);
+    wr[k] = buf_load16(rw, off[k]);
+  }
+
+  // ---- sum of squares: fp64 (exact for 16-bit inputs); waves added in ascending order
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    float xf[8];
+    unpack8<DT>(xr[k], xf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)xf[i], (double)xf[i], acc);
+  }
+  acc = group_sum<64>(acc);
+  if ((tid & 63) == 0) part[wave] = acc;
+  __syncthreads();
+  double tot = part[0];
+#pragma unroll
+  for (int v = 1; v < GWV; ++v) tot += part[v];
+  const float ssq = (float)tot;            // one rounding of the exact sum
+  const float rstd = rstd_of(ssq / (float)p.N + p.eps);
+
+  // ---- normalise: (x * rstd) * w, rounded to the input dtype
+  float y[KC][8];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    float xf[8], wf[8];
+    unpack8<DT>(xr[k], xf);
+    unpack8<DT>(wr[k], wf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[k][i] = DT::round((xf[i] * rstd) * wf[i]);
+  }
+
+  // ---- RoPE on the last R columns: pair p <-> p + R/2, through LDS
+  const uint32_t R = p.rope;
+  if (R > 0) {
+    const uint32_t half = R / 2, t0 = nch - R / 8, hc = R / 16;  // first tail chunk, chunks per half
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (ok[k] && ch[k] >= t0) {
+        float* d = tail_s + 8 * (ch[k] - t0);
+        *(float4*)d = make_float4(y[k][0], y[k][1], y[k][2], y[k][3]);
+        *(float4*)(d + 4) = make_float4(y[k][4], y[k][5], y[k][6], y[k][7]);
+      }
+    __syncthreads();
+    const size_t trow = (size_t)(row / p.rows_per_token) * half;
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (ok[k] && ch[k] >= t0) {
+        const uint32_t j = ch[k] - t0;
+        const bool lo_half = j < hc;
+        const uint32_t pj = lo_half ? j : j - hc;  // pair chunk index in [0, R/16)
+        const float* c8 = p.cos + trow + 8 * pj;
+        const float* s8 = p.sin + trow + 8 * pj;
+        const float4 ca = *(const float4*)c8, cb = *(const float4*)(c8 + 4);
+        const float4 sa = *(const float4*)s8, sb = *(const float4*)(s8 + 4);
+        const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+        const float ss[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+        const float* other = tail_s + 8 * (lo_half ? j + hc : j - hc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (lo_half) {
+            const float lo = y[k][i], hi = other[i];
+            y[k][i] = DT::round((lo * cc[i]) - (hi * ss[i]));
+          } else {
+            const float hi = y[k][i], lo = other[i];
+            y[k][i] = DT::round((hi * cc[i]) + (lo * ss[i]));
+          }
+        }
+      }
+  }
+
+  if (p.y != nullptr) {
+    const rsrc_t ry = make_rsrc(p.y + (size_t)row * p.N, row_bytes);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) buf_store16_nt(ry, off[k], pack8<DT>(y[k]));
+  }
+
+  // ---- per-group absmax, scale and codes
+  const uint32_t n_groups = p.N / p.group_size;
+  const rsrc_t rq = make_rsrc(p.codes + (size_t)row * p.N, p.N);
+  const rsrc_t rs = make_rsrc(p.scales + (size_t)row * n_groups, 4u * n_groups);
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
+    const float amax = group_max<GL>(m);
+    // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
+    float scale;
+    if (p.scale_by_rcp)
+      scale = amax >= 1e-4f ? div_by(amax, p.fp8_max, p.rcp_fp8_max) : p.scale_floor;
+    else
+      scale = fmaxf(amax, 1e-4f) / p.fp8_max;
+    const float rsc = rcp_rn(scale);
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = div_by(y[k][i], scale, rsc);
+    if (p.clamp) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -p.fp8_max, p.fp8_max);
+    }
+    uint2 cw;
+    cw.x = fp8x4(q[0], q[1], q[2], q[3], __float_as_uint(q[0]));
+    cw.y = fp8x4(q[4], q[5], q[6], q[7], __float_as_uint(q[4]));
+    buf_store8_nt(rq, ok[k] ? 8u * ch[k] : kOutOfRange, cw);
+    // the group's first lane stores its scale
+    const bool first = ok[k] && ch[k] % GL == 0;
+    buf_store4(rs, first ? 4u * (ch[k] / GL) : kOutOfRange, scale);
+  }
+}
+
+// --------------------------------------------------------------- launcher
+
+template <class DT, int KC>
+static hipError_t launch_kc(const GroupQuantParams& p, dim3 g, hipStream_t s) {
+  switch (p.group_size / 8) {
+    case 1: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 1>), g, dim3(GT), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 2>), g, dim3(GT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 4>), g, dim3(GT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 8>), g, dim3(GT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 16>), g, dim3(GT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 32>), g, dim3(GT), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 64>), g, dim3(GT), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class DT>
+static hipError_t launch_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
+  const uint32_t nch = p.N / 8;
+  if (nch <= GT) return launch_kc<DT, 1>(p, g, s);
+  if (nch <= 2 * GT) return launch_kc<DT, 2>(p, g, s);
+  if (nch <= 4 * GT) return launch_kc<DT, 4>(p, g, s);
+  if (nch <= 8 * GT) return launch_kc<DT, 8>(p, g, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  if (p.rope > kMaxRope) return hipErrorInvalidValue;
+  p.rcp_fp8_max = 1.0f / p.fp8_max;
+  p.scale_floor = 1e-4f / p.fp8_max;
+  p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;
+  p.clamp = fp8_clamp_needed(p.fp8_max) ? 1u : 0u;
+  const dim3 grid(p.M);
+  return bf16 ? launch_dt<BF16>(p, grid, stream) : launch_dt<F16>(p, grid, stream);
+}
+
+}  // namespace rnq

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -77,6 +78,51 @@ struct WideBwdParams {
   uint32_t blocks;
   float eps;
 };
+
+// RMSNorm -> partial RoPE -> FP8 with one scale per group of group_size
+// consecutive elements, over rows of up to 16384 elements (row r uses table
+// row r / rows_per_token).
+struct GroupQuantParams {
+  const uint16_t* x;
+  const uint16_t* w;
+  const float* cos;  // [M / rows_per_token, rope / 2]
+  const float* sin;
+  uint16_t* y;       // optional
+  uint8_t* codes;    // [M, N]
+  float* scales;     // [M, N / group_size]
+  uint32_t M;
+  uint32_t N;
+  uint32_t rope;
+  uint32_t rows_per_token;
+  uint32_t group_size;
+  float eps;
+  float fp8_max;
+  // filled by the launcher
+  float rcp_fp8_max;
+  float scale_floor;
+  uint32_t scale_by_rcp;
+  uint32_t clamp;
+};
+
+hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream);
+
+// Host side: e4m3fn code magnitude of a positive value below 480 (nearest even).
+inline int e4m3_magnitude_host(double v) {
+  if (v < 0x1p-6) return (int)nearbyint(v * 512.0);
+  int e = 0;
+  const double m = frexp(v, &e) * 2.0;  // v = m * 2^(e-1), m in [1, 2)
+  int mant = (int)nearbyint((m - 1.0) * 8.0);
+  int ex = e - 1;
+  if (mant == 8) { mant = 0; ++ex; }
+  return ((ex + 7) << 3) | mant;
+}
+
+// The clamp to +-fp8_max can only change a code when some quotient lands
+// above fp8_max; every |y / scale| is at most fp8_max * (1 + 2^-22), so the
+// clamp is needed only if that margin reaches a different code.
+inline bool fp8_clamp_needed(float fp8_max) {
+  return e4m3_magnitude_host((double)fp8_max * (1.0 + 0x1p-20)) != e4m3_magnitude_host((double)fp8_max);
+}
 
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);

@@ -1,29 +1,9 @@
 // Row-kernel launcher: host-side set-up shared by every mode (the kernel is
 // in rnq_rows.h; its modes are instantiated in rnq_rows_quant.hip and
 // rnq_rows_norm.hip).
-#include <math.h>
-
 #include "rnq_rows.h"
 
 namespace rnq {
-
-// e4m3fn code magnitude of a positive value below 480 (nearest even), host side.
-static int e4m3_magnitude(double v) {
-  if (v < 0x1p-6) return (int)nearbyint(v * 512.0);
-  int e = 0;
-  const double m = frexp(v, &e) * 2.0;  // v = m * 2^(e-1), m in [1, 2)
-  int mant = (int)nearbyint((m - 1.0) * 8.0);
-  int ex = e - 1;
-  if (mant == 8) { mant = 0; ++ex; }
-  return ((ex + 7) << 3) | mant;
-}
-
-// The clamp to +-fp8_max can only change a code when some quotient lands
-// above fp8_max; every |y / scale| is at most fp8_max * (1 + 2^-22), so the
-// clamp is needed only if that margin reaches a different code.
-static bool clamp_needed(float fp8_max) {
-  return e4m3_magnitude((double)fp8_max * (1.0 + 0x1p-20)) != e4m3_magnitude((double)fp8_max);
-}
 
 #ifndef RNQ_ROWS_TARGET_WAVES
 #define RNQ_ROWS_TARGET_WAVES 4096  // 4 per SIMD: what stays resident at the kernel's register use
@@ -58,7 +38,7 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.rcp_fp8_max = 1.0f / p.fp8_max;
   p.scale_floor = 1e-4f / p.fp8_max;
   p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;
-  p.clamp = quant && clamp_needed(p.fp8_max) ? 1u : 0u;
+  p.clamp = quant && fp8_clamp_needed(p.fp8_max) ? 1u : 0u;
   const int mode = (quant ? ROW_QUANT : 0) | (p.rope > 0 ? ROW_ROPE : 0) | (p.y0 != nullptr ? ROW_Y : 0) |
                    (p.rstd != nullptr ? ROW_RSTD : 0);
   switch (mode) {

@@ -283,6 +283,16 @@ def norm_rope_bytes(rows, width, rope_dim, rows_per_token=1, in_bytes=2) -> dict
     return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
 
 
+def grouped_bytes(rows, width, rope_dim, group_size, rows_per_token=1, in_bytes=2, write_y=False) -> dict:
+    """Bytes at the boundary of ``rnq_rmsnorm_rope_fp8_grouped``: x, the weight row and one
+    cos/sin row per token read once; one code per element, one fp32 scale per group and
+    (optionally) y written once."""
+    tables = rows // rows_per_token
+    reads = rows * width * in_bytes + width * in_bytes + 2 * tables * (rope_dim // 2) * 4
+    writes = rows * width + rows * (width // group_size) * 4 + (rows * width * in_bytes if write_y else 0)
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
 def rmsnorm_fwd_bytes(rows, width, in_bytes=2, write_rstd=False) -> dict:
     reads = rows * width * in_bytes + width * in_bytes
     writes = rows * width * in_bytes + (rows * 4 if write_rstd else 0)

@@ -122,6 +122,28 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
                             float eps, int dtype, void* stream);
 
 /*
+ * RMSNorm + partial NeoX RoPE + FP8 with one scale per group (chapter 13
+ * fusion page, rms_norm_rope_quant_fused: every group_size consecutive
+ * elements of a row share one scale):
+ *   y     = RMSNorm + RoPE as rnq_rmsnorm_rope (row m uses table row
+ *           m / rows_per_token), rounded to dtype
+ *   for every group g of row m (elements g*group_size .. (g+1)*group_size-1):
+ *     scale[m,g] = max(max |y| over the group, 1e-4) / fp8_max    (fp32)
+ *     code       = e4m3fn(clamp(y / scale[m,g], -fp8_max, fp8_max))  (nearest even)
+ * x [M,N] in dtype; w [N]; cos, sin [M/rows_per_token, R/2] fp32 (NULL allowed
+ * when R == 0); outputs codes [M,N] bytes (8-byte aligned), scales
+ * [M, N/group_size] fp32, y [M,N] in dtype (optional, NULL = not written).
+ * Requirements: N a multiple of 8, at most 16384; group_size a power of two in
+ * [8, 512] dividing N (SHAPE if it does not divide, UNSUPPORTED otherwise);
+ * R = rope_dim a multiple of 16, R <= N, R <= 1024; M % rows_per_token == 0;
+ * 0 < fp8_max <= 448; M < 2^31. 16-bit tensors and the table 16-byte aligned.
+ */
+rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const float* cos, const float* sin,
+                                        void* y, uint8_t* codes, float* scales, int64_t M, int64_t N,
+                                        int64_t rope_dim, int64_t rows_per_token, int64_t group_size, float eps,
+                                        float fp8_max, int dtype, void* stream);
+
+/*
  * QK-norm + partial NeoX RoPE + per-row FP8 (chapter 28 page, the prologue;
  * chapter 13 fusion page, rms_norm_rope_quant_fused with one group per row):
  *   for every (token t, head h) row of q [T,Hq,D] (weight wq) and of

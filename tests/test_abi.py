@@ -116,3 +116,32 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("RNQ_LIBRARY", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         rnq.load_library()
+
+
+def test_grouped_argument_validation():
+    lib = _lib()
+
+    def call(x=FAKE, cos=FAKE, codes=FAKE, scales=FAKE, M=4, N=4096, R=128, rpt=1, g=128, eps=1e-6, fmax=448.0):
+        return lib.rnq_rmsnorm_rope_fp8_grouped(x, FAKE, cos, cos, None, codes, scales, M, N, R, rpt, g, eps, fmax,
+                                                0, None)
+
+    assert call(x=None) == 1
+    assert call(scales=None) == 1
+    assert call(cos=None) == 1
+    assert call(M=0, x=None) == 0  # zero rows: nothing launched, no pointer checked
+    assert call(M=-1) == 2
+    assert call(g=96) == 2  # does not divide 4096
+    assert call(N=384, g=48) == 3  # divides, not a power of two
+    assert call(N=8192, g=1024) == 3  # above 512
+    assert call(N=4096, g=4) == 3  # below 8
+    assert call(N=16392, g=8) == 3  # row too wide
+    assert call(N=4100, g=4100, R=0) == 3  # divides, not a power of two
+    assert call(R=2048) == 3  # rope tail above 1024
+    assert call(R=24) == 3  # not a multiple of 16
+    assert call(R=130) == 3
+    assert call(R=131) == 2  # odd
+    assert call(M=6, rpt=4) == 2  # rows not a multiple of rows_per_token
+    assert call(rpt=0) == 2
+    assert call(fmax=500.0) == 4
+    assert call(eps=-1.0) == 4
+    assert call(N=384, g=48) == 3 and b"power of two" in lib.rnq_last_error()

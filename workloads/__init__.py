@@ -14,6 +14,9 @@ where M = tokens x heads, weight ``[N]``, cos/sin ``[tokens, rope_dim/2]``):
 * ``norm_rope_fp16`` - 16384 rows x 128, rope 64, fp16 x = 2*N(0,1), random positions
 * ``qk_4k``      - 4096 tokens x (32 q + 8 kv) heads x 128, full rope, 1% outliers x20
 * ``qk_64k``     - 65536 tokens x (64 q + 8 kv) heads x 128, full rope, theta = 1e6
+* ``grouped_small`` - 256 rows x 4096, rope 128, fp16, one scale per 128 elements
+  (the shape of the fusion page's own check of its per-group kernel)
+* ``grouped_4k`` - 4096 rows x 4096, rope 128, bf16, one scale per 128 elements, y written
 """
 
 from __future__ import annotations
@@ -37,7 +40,7 @@ __all__ = [
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "qk" (norm+rope+fp8), "norm_rope", "rmsnorm"
+    kind: str  # "qk" (norm+rope+fp8), "norm_rope", "rmsnorm", "grouped" (norm+rope+per-group fp8)
     seed: int
     tokens: int = 0
     q_heads: int = 0
@@ -55,6 +58,7 @@ class Workload:
     write_y: bool = False
     x_std: float = 1.0
     positions: str = "index"  # "index" (pos = token/row index) or "random:<hi>"
+    group_size: int = 0  # grouped: elements per scale
     description: str = ""
 
 
@@ -84,6 +88,16 @@ WORKLOADS: dict[str, Workload] = {
             "qk_64k", "qk", seed=1005, tokens=65536, q_heads=64, kv_heads=8, head_dim=128,
             rope_dim=128, theta=1e6,
             description="QK-norm + RoPE + FP8, 65536 tokens x (64+8) heads x 128, bf16, theta 1e6",
+        ),
+        Workload(
+            "grouped_small", "grouped", seed=1006, rows=256, width=4096, rope_dim=128, dtype="fp16",
+            group_size=128, write_y=True,
+            description="RMSNorm + RoPE + per-group FP8, 256 x 4096, rope 128, fp16, groups of 128",
+        ),
+        Workload(
+            "grouped_4k", "grouped", seed=1007, rows=4096, width=4096, rope_dim=128, group_size=128,
+            write_y=True,
+            description="RMSNorm + RoPE + per-group FP8, 4096 x 4096, rope 128, bf16, groups of 128, y written",
         ),
     ]
 }
@@ -153,7 +167,7 @@ def generate(name_or_wl, *, tokens: int | None = None, seed: int | None = None) 
             cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
             tokens=T, q_heads=Hq, kv_heads=Hk, head_dim=D, rope_dim=wl.rope_dim,
         )
-    elif wl.kind == "norm_rope":
+    elif wl.kind in ("norm_rope", "grouped"):
         M = wl.rows if tokens is None else tokens
         N = wl.width
         x = _normal((M, N), g, wl.x_std)
@@ -162,7 +176,7 @@ def generate(name_or_wl, *, tokens: int | None = None, seed: int | None = None) 
         cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
         out.update(
             x=x.to(dt), w=w.to(dt), cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
-            rows=M, width=N, rope_dim=wl.rope_dim, rows_per_token=1,
+            rows=M, width=N, rope_dim=wl.rope_dim, rows_per_token=1, group_size=wl.group_size,
         )
     elif wl.kind == "rmsnorm":
         M = wl.rows if tokens is None else tokens
