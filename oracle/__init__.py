@@ -47,12 +47,12 @@ from .prologue import (
     rmsnorm_rope_fp8_grouped,
     truth_norm_rope,
 )
-from .backward import rmsnorm_bwd
+from .backward import rmsnorm_bwd, rope_bwd_rotate, rmsnorm_rope_bwd
 
 __all__ = [
     "bf16_round", "bf16_to_f32", "f16_round", "f16_to_f32", "e4m3_encode", "e4m3_decode",
     "E4M3_TABLE", "dtype_round", "dtype_to_f32", "sum_squares_f32", "sum_squares_exact_mask",
     "rmsnorm_fwd", "rope_tail", "quantize_rows", "norm_rope_quant_rows", "qk_norm_rope_fp8",
     "rmsnorm_rope", "truth_norm_rope", "rmsnorm_bwd",
-    "quantize_groups", "rmsnorm_rope_fp8_grouped",
+    "quantize_groups", "rmsnorm_rope_fp8_grouped", "rope_bwd_rotate", "rmsnorm_rope_bwd",
 ]

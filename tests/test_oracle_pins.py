@@ -310,6 +310,111 @@ def test_backward_single_row_dw():
     np.testing.assert_allclose(dw, g * x * rstd[0], rtol=1e-15)
 
 
+# ------------------------------------------------------- RoPE backward pins
+
+
+def _loss_norm_rope_complex(x, w, gy, c, s, eps):
+    """sum(gy * y) for y = RoPE(RMSNorm(x)) in real arithmetic; the tail pairs
+    rotated as complex numbers (lo + i hi) * (c + i s)."""
+    N, half = x.shape[-1], c.shape[-1]
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=-1) + eps)
+    n = x * rstd[:, None] * w[None, :]
+    z = (n[:, N - 2 * half : N - half] + 1j * n[:, N - half :]) * (c + 1j * s)
+    y = np.concatenate([n[:, : N - 2 * half], z.real, z.imag], axis=1)
+    return float((gy * y).sum())
+
+
+def _rope_bwd_case(M=3, N=16, R=8, seed=71, rows_per_token=1):
+    rng = np.random.default_rng(seed)
+    xb = _bf16(rng.standard_normal((M, N)))
+    wb = _bf16(1 + 0.3 * rng.standard_normal(N))
+    gb = _bf16(rng.standard_normal((M, N)))
+    c, s = _table(M // rows_per_token, R // 2, seed + 1)
+    return xb, wb, gb, c, s
+
+
+def test_rope_backward_matches_central_differences():
+    M, N, R = 3, 16, 8
+    xb, wb, gb, c, s = _rope_bwd_case(M, N, R)
+    eps = float(np.float32(1e-6))
+    dx, dw, _ = oracle.rmsnorm_rope_bwd(xb, wb, gb, c, s, 1e-6)
+    x = codecs.bf16_to_f32(xb).astype(np.float64)
+    w = codecs.bf16_to_f32(wb).astype(np.float64)
+    g = codecs.bf16_to_f32(gb).astype(np.float64)
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    h = 1e-6
+
+    def loss(xx, ww):
+        return _loss_norm_rope_complex(xx, ww, g, c64, s64, eps)
+
+    fd_x = np.zeros_like(x)
+    for i in range(M):
+        for j in range(N):
+            xp = x.copy(); xp[i, j] += h
+            xm = x.copy(); xm[i, j] -= h
+            fd_x[i, j] = (loss(xp, w) - loss(xm, w)) / (2 * h)
+    fd_w = np.zeros_like(w)
+    for j in range(N):
+        wp = w.copy(); wp[j] += h
+        wm = w.copy(); wm[j] -= h
+        fd_w[j] = (loss(x, wp) - loss(x, wm)) / (2 * h)
+    np.testing.assert_allclose(dx, fd_x, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dw, fd_w, rtol=1e-6, atol=1e-8)
+
+
+def test_rope_backward_matches_torch_autograd_float64():
+    """Library routine: torch's reverse-mode AD of the same map, complex rotation, float64."""
+    M, N, R = 6, 64, 32
+    xb, wb, gb, c, s = _rope_bwd_case(M, N, R, seed=72)
+    dx, dw, _ = oracle.rmsnorm_rope_bwd(xb, wb, gb, c, s, 1e-6)
+    x = torch.tensor(codecs.bf16_to_f32(xb), dtype=torch.float64, requires_grad=True)
+    w = torch.tensor(codecs.bf16_to_f32(wb), dtype=torch.float64, requires_grad=True)
+    g = torch.tensor(codecs.bf16_to_f32(gb), dtype=torch.float64)
+    rot = torch.complex(torch.tensor(c, dtype=torch.float64), torch.tensor(s, dtype=torch.float64))
+    n = x * torch.rsqrt((x * x).mean(-1, keepdim=True) + float(np.float32(1e-6))) * w
+    z = torch.complex(n[:, N - R : N - R // 2], n[:, N - R // 2 :]) * rot
+    y = torch.cat([n[:, : N - R], z.real, z.imag], dim=1)
+    (y * g).sum().backward()
+    np.testing.assert_allclose(dx, x.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dw, w.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_rope_backward_special_cases_reduce_to_rmsnorm_backward():
+    xb, wb, gb, c, s = _rope_bwd_case(5, 32, 16, seed=73)
+    ref = oracle.rmsnorm_bwd(xb, wb, gb, 1e-6)
+    # no rope tail
+    z = np.zeros((5, 0), F32)
+    out = oracle.rmsnorm_rope_bwd(xb, wb, gb, z, z, 1e-6)
+    assert all(np.array_equal(a, b) for a, b in zip(out, ref))
+    # identity rotation (cos 1, sin 0)
+    out = oracle.rmsnorm_rope_bwd(xb, wb, gb, np.ones_like(c), np.zeros_like(s), 1e-6)
+    assert all(np.array_equal(a, b) for a, b in zip(out, ref))
+
+
+def test_rope_backward_rotation_is_orthogonal_and_inverts_the_forward():
+    rng = np.random.default_rng(74)
+    M, N, half = 4, 24, 8
+    g = rng.standard_normal((M, N))
+    c, s = _table(M, half, 75)
+    gn = oracle.rope_bwd_rotate(g, c, s)
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    k = c64 * c64 + s64 * s64  # 1 up to the fp32 rounding of the table
+    lo, hi = g[:, N - 2 * half : N - half], g[:, N - half :]
+    glo, ghi = gn[:, N - 2 * half : N - half], gn[:, N - half :]
+    np.testing.assert_allclose(glo**2 + ghi**2, (lo**2 + hi**2) * k, rtol=1e-12)
+    # rotating back by the forward map gives k * g
+    np.testing.assert_allclose(glo * c64 - ghi * s64, k * lo, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(ghi * c64 + glo * s64, k * hi, rtol=1e-12, atol=1e-15)
+    assert np.array_equal(gn[:, : N - 2 * half], g[:, : N - 2 * half])
+
+
+def test_rope_backward_rows_per_token_shares_the_table_row():
+    xb, wb, gb, c, s = _rope_bwd_case(8, 32, 16, seed=76, rows_per_token=4)
+    a = oracle.rmsnorm_rope_bwd(xb, wb, gb, c, s, 1e-6, rows_per_token=4)
+    b = oracle.rmsnorm_rope_bwd(xb, wb, gb, np.repeat(c, 4, axis=0), np.repeat(s, 4, axis=0), 1e-6)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
 # ----------------------------------------------------- consistency with the pages' torch code
 
 
