@@ -157,6 +157,28 @@ def bench_grouped(torch, rnq, workloads, ledger, name, steps, warmup):
     return {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
 
 
+def bench_rope_bwd(torch, rnq, workloads, ledger, name, steps, warmup):
+    d = workloads.generate(name)
+    M, N, R, rpt = d["rows"], d["width"], d["rope_dim"], d["rows_per_token"]
+    led = ledger.rope_bwd_bytes(M, N, R, rpt)
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(led["total"])
+    ws_bytes = rnq.rnq_rmsnorm_bwd_workspace_size(M, N)
+    g = torch.Generator("cpu").manual_seed(91)
+    gy = torch.randn(d["x"].shape, generator=g).to(d["x"].dtype)
+    sets = [{"x": d["x"].to(dev), "gy": gy.to(dev), "cos": d["cos"].to(dev), "sin": d["sin"].to(dev),
+             "gx": torch.empty_like(d["x"], device=dev), "gw": torch.empty((N,), dtype=torch.float32, device=dev),
+             "ws": torch.empty((max(ws_bytes, 16) // 4,), dtype=torch.float32, device=dev)} for _ in range(n_sets)]
+    w = d["w"].to(dev)
+    launches = [rnq.prepare_rmsnorm_rope_bwd(s["x"], w, s["gy"], s["cos"], s["sin"], s["gx"], s["gw"], s["ws"],
+                                             rows_per_token=rpt) for s in sets]
+    ms = _timed(torch, launches, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": name + " rope bwd", "ms": ms, "bytes": led["total"], "rows": M, "sets": n_sets,
+            "workspace_bytes_each_way": ws_bytes}
+
+
 def bench_rmsnorm(torch, rnq, workloads, ledger, name, steps, warmup):
     d = workloads.generate(name)
     M, N = d["rows"], d["width"]
@@ -320,6 +342,7 @@ def main() -> int:
         paths += [_summary(r) for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, warm)]
         paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
         paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
+        paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 20)))
         out["other_paths"] = paths
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)

@@ -29,16 +29,19 @@ __all__ = [
     "rnq_rmsnorm_bwd",
     "rnq_rmsnorm_bwd_workspace_size",
     "rnq_rmsnorm_rope_fp8_grouped",
+    "rnq_rmsnorm_rope_bwd",
     "prepare_qk_norm_rope_fp8",
     "prepare_rmsnorm_rope_fp8_grouped",
     "prepare_rmsnorm_rope",
     "prepare_rmsnorm_fwd",
     "prepare_rmsnorm_bwd",
+    "prepare_rmsnorm_rope_bwd",
     "qk_norm_rope_fp8",
     "rmsnorm",
     "rmsnorm_bwd",
     "rmsnorm_rope",
     "rmsnorm_rope_fp8_grouped",
+    "rmsnorm_rope_bwd",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -53,6 +56,7 @@ EXPORTED_SYMBOLS = (
     "rnq_rmsnorm_rope",
     "rnq_qk_norm_rope_fp8",
     "rnq_rmsnorm_rope_fp8_grouped",
+    "rnq_rmsnorm_rope_bwd",
 )
 
 RNQ_BF16 = 0
@@ -102,6 +106,8 @@ def load_library():
     lib.rnq_qk_norm_rope_fp8.restype = i32
     lib.rnq_rmsnorm_rope_fp8_grouped.argtypes = [vp] * 7 + [i64] * 5 + [f32, f32, i32, vp]
     lib.rnq_rmsnorm_rope_fp8_grouped.restype = i32
+    lib.rnq_rmsnorm_rope_bwd.argtypes = [vp] * 9 + [ctypes.c_size_t] + [i64] * 4 + [f32, i32, vp]
+    lib.rnq_rmsnorm_rope_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -277,6 +283,33 @@ def prepare_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, e
     return _launcher(lib.rnq_rmsnorm_bwd, args)
 
 
+def rnq_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, rstd=None, *, rows_per_token: int = 1,
+                         eps: float = 1e-6, stream=None) -> None:
+    """Backward of rnq_rmsnorm_rope into caller-provided grad_x, grad_w (fp32) and workspace."""
+    prepare_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, rstd, rows_per_token=rows_per_token,
+                             eps=eps, stream=stream)()
+
+
+def prepare_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, rstd=None, *,
+                             rows_per_token: int = 1, eps: float = 1e-6, stream=None):
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    half = 0 if cos is None else cos.shape[-1]
+    _expect(w, x.dtype, (N,), "w")
+    _expect(grad_y, x.dtype, (M, N), "grad_y")
+    _expect(grad_x, x.dtype, (M, N), "grad_x")
+    _expect(grad_w, torch.float32, (N,), "grad_w")
+    _expect(rstd, torch.float32, (M,), "rstd")
+    if cos is not None:
+        _expect(cos, torch.float32, (M // max(rows_per_token, 1), half), "cos")
+        _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(cos), _ptr(sin), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
+            _ptr(workspace), ws_bytes, M, N, 2 * half, rows_per_token, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_rope_bwd, args)
+
+
 def rnq_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, group_size: int = 128,
                                  rows_per_token: int = 1, eps: float = 1e-6, fp8_max: float = 448.0,
                                  stream=None) -> None:
@@ -342,6 +375,17 @@ def rmsnorm_bwd(x, w, grad_y, rstd=None, *, eps=1e-6):
     gw = torch.empty((N,), dtype=torch.float32, device=x.device)
     ws = torch.empty((max(rnq_rmsnorm_bwd_workspace_size(M, N), 16) // 4,), dtype=torch.float32, device=x.device)
     rnq_rmsnorm_bwd(x, w, grad_y, gx, gw, ws, rstd, eps=eps)
+    return gx, gw
+
+
+def rmsnorm_rope_bwd(x, w, grad_y, cos, sin, rstd=None, *, rows_per_token=1, eps=1e-6):
+    """Returns (grad_x, grad_w fp32) of rmsnorm_rope."""
+    torch = _torch()
+    M, N = x.shape
+    gx = torch.empty_like(x)
+    gw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    ws = torch.empty((max(rnq_rmsnorm_bwd_workspace_size(M, N), 16) // 4,), dtype=torch.float32, device=x.device)
+    rnq_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, gx, gw, ws, rstd, rows_per_token=rows_per_token, eps=eps)
     return gx, gw
 
 

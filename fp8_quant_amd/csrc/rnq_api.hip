@@ -286,21 +286,35 @@ size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
   return (size_t)bwd_blocks(M, N) * (size_t)N * sizeof(float);
 }
 
-rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, const float* rstd,
-                           void* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
-                           int64_t M, int64_t N, float eps, int dtype, void* stream) {
+}  // extern "C"
+
+namespace rnq {
+
+// Shared by the two backward entry points: validation, then the narrow-row
+// kernel for widths 64..512 (with or without the RoPE tail) or the wide one.
+static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void* w, const void* grad_y,
+                                     const float* cos, const float* sin, const float* rstd, void* grad_x,
+                                     float* grad_w, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                                     int64_t rope_dim, int64_t rows_per_token, float eps, int dtype, void* stream) {
   rnq_status s;
   if ((s = check_dtype(dtype)) != RNQ_OK) return s;
   if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
   if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
+  if (rope_dim > 0 && !narrow_bwd_width(N))
+    return fail(RNQ_ERR_UNSUPPORTED, "the RoPE backward takes rows of 64, 128, 256 or 512 (got %lld)", (long long)N);
+  if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
+  if (M % rows_per_token != 0)
+    return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
   if (M == 0 || N == 0) return ok();
   if (!x || !w || !grad_y || !grad_x || !grad_w) return fail(RNQ_ERR_NULL, "x, w, grad_y, grad_x and grad_w are required");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
   const size_t need = rnq_rmsnorm_bwd_workspace_size(M, N);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(RNQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes, workspace);
-  const void* a16[] = {x, w, grad_y, grad_x, grad_w, workspace};
+  const void* a16[] = {x, w, grad_y, grad_x, grad_w, workspace, cos, sin};
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
   if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
@@ -318,7 +332,37 @@ rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, con
   p.blocks = bwd_blocks(M, N);
   p.rows_per_block = (uint32_t)((M + p.blocks - 1) / p.blocks);
   p.eps = eps;
-  return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_bwd");
+  if (!narrow_bwd_width(N)) return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
+
+  // the narrow kernel addresses a block's rows and the tables with 32-bit offsets
+  const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;
+  if ((int64_t)p.rows_per_block * N * 2 >= ((int64_t)1 << 31) || table_bytes >= ((int64_t)1 << 31))
+    return fail(RNQ_ERR_UNSUPPORTED, "a block's rows or the cos/sin table exceed 2 GiB");
+  p.cos = cos;
+  p.sin = sin;
+  p.rope = (uint32_t)rope_dim;
+  p.rows_per_token = (uint32_t)rows_per_token;
+  p.table_bytes = (uint32_t)table_bytes;
+  return hip_status(launch_narrow_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
+}
+
+}  // namespace rnq
+
+extern "C" {
+
+rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, const float* rstd,
+                           void* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
+                           int64_t M, int64_t N, float eps, int dtype, void* stream) {
+  return rmsnorm_bwd_common("rnq_rmsnorm_bwd", x, w, grad_y, nullptr, nullptr, rstd, grad_x, grad_w, workspace,
+                            workspace_bytes, M, N, 0, 1, eps, dtype, stream);
+}
+
+rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y, const float* cos, const float* sin,
+                                const float* rstd, void* grad_x, float* grad_w, void* workspace,
+                                size_t workspace_bytes, int64_t M, int64_t N, int64_t rope_dim,
+                                int64_t rows_per_token, float eps, int dtype, void* stream) {
+  return rmsnorm_bwd_common("rnq_rmsnorm_rope_bwd", x, w, grad_y, cos, sin, rstd, grad_x, grad_w, workspace,
+                            workspace_bytes, M, N, rope_dim, rows_per_token, eps, dtype, stream);
 }
 
 }  // extern "C"

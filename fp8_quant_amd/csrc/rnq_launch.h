@@ -77,6 +77,15 @@ struct WideBwdParams {
   uint32_t rows_per_block;
   uint32_t blocks;
   float eps;
+  // the gradient goes back through the RoPE of the last `rope` columns first
+  // (narrow rows only; rope == 0: plain RMSNorm backward)
+  const float* cos;  // [M / rows_per_token, rope / 2]
+  const float* sin;
+  uint32_t rope;
+  uint32_t rows_per_token;
+  uint32_t div_magic;   // row / rows_per_token = (row * div_magic) >> div_shift
+  uint32_t div_shift;
+  uint32_t table_bytes;  // bytes of one table (cos or sin)
 };
 
 // RMSNorm -> partial RoPE -> FP8 with one scale per group of group_size
@@ -127,5 +136,10 @@ inline bool fp8_clamp_needed(float fp8_max) {
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);
 hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream);
+// grad_w[j] = sum over b of partial[b, j] in a fixed order
+hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream);
+// rows of 64, 128, 256 or 512 elements, several per wave; rope optional
+bool narrow_bwd_width(int64_t N);
+hipError_t launch_narrow_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
 
 }  // namespace rnq

@@ -14,7 +14,7 @@
 // Backward grad_w is deterministic: workgroup b owns a fixed contiguous range
 // of rows and accumulates grad_y * xn for its columns in registers, in row
 // order; the per-workgroup partials go to the caller's workspace [blocks, N];
-// a second kernel adds them per column in a fixed order (see dw_reduce_kernel).
+// a second kernel adds them per column in a fixed order (dw_reduce_kernel).
 #include "rnq_device.h"
 #include "rnq_launch.h"
 
@@ -258,35 +258,34 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   }
 }
 
-// grad_w[j] = sum over b of partial[b, j] in a fixed order. A workgroup owns
-// RQ float4 column groups; its RP row phases each add partial rows phase,
-// phase + RP, ... in ascending order, then the phase sums are added in
-// ascending phase order. RQ = 4 gives N / 16 workgroups (256 at N = 4096).
-constexpr int RQ = 4;   // column float4 groups per workgroup
-constexpr int RP = 64;  // row phases
-__global__ __launch_bounds__(RQ * RP) void dw_reduce_kernel(const float* __restrict__ partial, float* __restrict__ gw,
-                                                           uint32_t blocks, uint32_t N) {
-  __shared__ float4 acc_s[RP][RQ];
-  const uint32_t cq = threadIdx.x % RQ, ph = threadIdx.x / RQ;
-  const uint32_t c4 = blockIdx.x * RQ + cq;  // float4 column group
-  const bool ok = 4 * c4 < N;
+// grad_w[j] = sum over b of partial[b, j] in a fixed order. One wave per
+// float4 column group: lane l adds the partial rows l, l + 64, l + 128, ...
+// in ascending order (RU rows' loads in flight at a time; rows past the last
+// are outside the buffer descriptor and read as zero), then the 64 lane sums
+// are added by a fixed xor butterfly.
+constexpr int RDW = 4;  // waves (column groups) per workgroup
+constexpr int RU = 8;   // partial rows in flight per lane
+__global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __restrict__ partial, float* __restrict__ gw,
+                                                            uint32_t blocks, uint32_t N) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t c4 = blockIdx.x * RDW + (threadIdx.x >> 6);  // float4 column group (wave-uniform)
+  if (4 * c4 >= N) return;
+  const rsrc_t rp = make_rsrc(partial, 4u * blocks * N);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (ok) {
-    for (uint32_t b = ph; b < blocks; b += RP) {
-      const float4 v = *(const float4*)(partial + (size_t)b * N + 4 * (size_t)c4);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  for (uint32_t b0 = 0; b0 < blocks; b0 += 64 * RU) {
+    float4 v[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) v[u] = buf_load16f(rp, 4u * ((b0 + 64u * u + lane) * N + 4u * c4));
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
     }
   }
-  acc_s[ph][cq] = acc;
-  __syncthreads();
-  if (ph == 0 && ok) {
-    float4 t = acc_s[0][cq];
-    for (int i = 1; i < RP; ++i) {
-      const float4 v = acc_s[i][cq];
-      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
-    }
-    *(float4*)(gw + 4 * (size_t)c4) = t;
-  }
+  acc.x = group_sum<64>(acc.x);
+  acc.y = group_sum<64>(acc.y);
+  acc.z = group_sum<64>(acc.z);
+  acc.w = group_sum<64>(acc.w);
+  if (lane == 0) *(float4*)(gw + 4 * (size_t)c4) = acc;
 }
 
 // ----------------------------------------------------------------- launchers
@@ -358,9 +357,12 @@ hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream
   const int kc = chunks_per_lane(p.N, p.N > 2048 ? 512 : 256);
   hipError_t e = bf16 ? bwd_kc<BF16>(p, kc, grid, stream) : bwd_kc<F16>(p, kc, grid, stream);
   if (e != hipSuccess) return e;
-  const uint32_t cols4 = p.N / 4;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((cols4 + RQ - 1) / RQ), dim3(RQ * RP), 0, stream,
-                     (const float*)p.partial, p.gw, p.blocks, p.N);
+  return launch_dw_reduce(p.partial, p.gw, p.blocks, p.N, stream);
+}
+
+hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream) {
+  const uint32_t cols4 = N / 4;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((cols4 + RDW - 1) / RDW), dim3(64 * RDW), 0, stream, partial, gw, blocks, N);
   return hipGetLastError();
 }
 

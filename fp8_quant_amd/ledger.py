@@ -299,6 +299,16 @@ def rmsnorm_fwd_bytes(rows, width, in_bytes=2, write_rstd=False) -> dict:
     return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
 
 
+def rope_bwd_bytes(rows, width, rope_dim, rows_per_token=1, in_bytes=2) -> dict:
+    """Bytes at the boundary of ``rnq_rmsnorm_rope_bwd`` (rstd recomputed): x and grad_y
+    read, the weight row and one cos/sin row per token read once, grad_x and fp32 grad_w
+    written (the workspace, the method's own overhead, is reported apart)."""
+    tables = rows // rows_per_token
+    reads = 2 * rows * width * in_bytes + width * in_bytes + 2 * tables * (rope_dim // 2) * 4
+    writes = rows * width * in_bytes + width * 4
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
 def rmsnorm_bwd_bytes(rows, width, in_bytes=2, read_rstd=False) -> dict:
     reads = 2 * rows * width * in_bytes + width * in_bytes + (rows * 4 if read_rstd else 0)
     writes = rows * width * in_bytes + width * 4

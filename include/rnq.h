@@ -122,6 +122,30 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
                             float eps, int dtype, void* stream);
 
 /*
+ * Backward of rnq_rmsnorm_rope (the rotation of the chapter 13 fusion page
+ * followed back, then the chapter 17 RMSNorm backward). The two casts to
+ * `dtype` in the forward count as identities. On the last R = rope_dim
+ * columns the output gradient goes through the transposed rotation, for
+ * p < R/2 with c = cos[t,p], s = sin[t,p], t = m / rows_per_token:
+ *   gn[N-R+p]     = grad_y[N-R+p] * c + grad_y[N-R+R/2+p] * s
+ *   gn[N-R+R/2+p] = grad_y[N-R+R/2+p] * c - grad_y[N-R+p] * s
+ * (gn = grad_y elsewhere; fp32), then, as rnq_rmsnorm_bwd with gn for grad_y:
+ *   grad_x = round_dtype(rstd * (gn * w - xn * C)), C = sum_j(gn * w * xn) / N
+ *   grad_w = sum over rows of gn * xn                  [N] fp32
+ * Layouts, rstd (NULL: recomputed), the workspace (rnq_rmsnorm_bwd_workspace_size(M, N)
+ * bytes) and the fixed-order grad_w reduction are those of rnq_rmsnorm_bwd;
+ * cos, sin and rows_per_token those of rnq_rmsnorm_rope.
+ * Requirements: N in {64, 128, 256, 512} when rope_dim > 0 (any width
+ * rnq_rmsnorm_bwd takes when rope_dim == 0); R a multiple of 16 with R <= N;
+ * M % rows_per_token == 0. cos/sin may be NULL when R == 0.
+ */
+rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y, const float* cos,
+                                const float* sin, const float* rstd, void* grad_x, float* grad_w,
+                                void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                                int64_t rope_dim, int64_t rows_per_token, float eps, int dtype,
+                                void* stream);
+
+/*
  * RMSNorm + partial NeoX RoPE + FP8 with one scale per group (chapter 13
  * fusion page, rms_norm_rope_quant_fused: every group_size consecutive
  * elements of a row share one scale):

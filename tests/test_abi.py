@@ -145,3 +145,42 @@ def test_grouped_argument_validation():
     assert call(fmax=500.0) == 4
     assert call(eps=-1.0) == 4
     assert call(N=384, g=48) == 3 and b"power of two" in lib.rnq_last_error()
+
+
+def test_rope_bwd_argument_validation():
+    lib = _lib()
+    need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 128)
+
+    def call(x=FAKE, cos=FAKE, ws=FAKE, wsb=need, M=4096, N=128, R=64, rpt=1, eps=1e-6, dt=0):
+        return lib.rnq_rmsnorm_rope_bwd(x, FAKE, FAKE, cos, cos, None, FAKE, FAKE, ws, wsb, M, N, R, rpt, eps, dt,
+                                        None)
+
+    assert call(x=None) == 1
+    assert call(cos=None) == 1
+    assert call(M=0, x=None) == 0
+    assert call(N=1024, R=64) == 3  # the RoPE backward takes narrow rows only
+    assert call(N=4100, R=0) == 3
+    assert call(R=24) == 3
+    assert call(R=63) == 2
+    assert call(R=256) == 2  # wider than the row
+    assert call(M=4095, rpt=2) == 2
+    assert call(rpt=0) == 2
+    assert call(wsb=need - 1) == 5
+    assert call(ws=None) == 5
+    assert call(eps=float("nan")) == 4
+    assert call(dt=7) == 4
+
+
+def test_autograd_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    from fp8_quant_amd import autograd as rag
+
+    if not os.path.exists(rnq.library_path()):
+        pytest.skip("librnq.so not built")
+    x = torch.randn(4, 128, dtype=torch.bfloat16, requires_grad=True)
+    w = torch.ones(128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        rag.rmsnorm(x, w)
+    cos = torch.ones(4, 32)
+    with pytest.raises(ValueError, match="GPU"):
+        rag.rmsnorm_rope(x, w, cos, torch.zeros(4, 32))
