@@ -92,24 +92,40 @@ def bench_qk(torch, rnq, workloads, ledger, name, steps, warmup):
     d = workloads.generate(name)
     T, Hq, Hk, D, R = d["tokens"], d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"]
     led = ledger.qk_bytes(T, Hq, Hk, D, R, write_y=wl.write_y)
+    pos_cpu = d.get("positions")
+    if pos_cpu is not None:
+        led = ledger.gathered_table_adjust(led, T, R, len(set(pos_cpu.tolist())))
     dev = torch.device("cuda:0")
     n_sets = _n_sets(led["total"])
     sets = []
     for _ in range(n_sets):
-        s = {"q": d["q"].to(dev), "k": d["k"].to(dev) if Hk else None,
+        if wl.fused_qkv:
+            # q and k are views into one fused projection output (v columns are not read)
+            qkv = d["qkv"].to(dev)
+            q, k = qkv[:, : Hq * D].view(T, Hq, D), qkv[:, Hq * D : (Hq + Hk) * D].view(T, Hk, D)
+        else:
+            q, k = d["q"].to(dev), d["k"].to(dev) if Hk else None
+        s = {"q": q, "k": k,
              "q8": torch.empty((T, Hq, D), dtype=torch.uint8, device=dev),
              "k8": torch.empty((T, Hk, D), dtype=torch.uint8, device=dev) if Hk else None,
              "qs": torch.empty((T, Hq), dtype=torch.float32, device=dev),
              "ks": torch.empty((T, Hk), dtype=torch.float32, device=dev) if Hk else None}
-        s["qy"] = torch.empty_like(s["q"]) if wl.write_y else None
+        s["qy"] = torch.empty((T, Hq, D), dtype=q.dtype, device=dev) if wl.write_y else None
         sets.append(s)
     wq = d["wq"].to(dev)
     wk = d["wk"].to(dev) if Hk else None
     cos, sin = d["cos"].to(dev), d["sin"].to(dev)
+    pos = None if pos_cpu is None else pos_cpu.to(dev)
     del d
 
-    launches = [rnq.prepare_qk_norm_rope_fp8(s["q"], s["k"], wq, wk, cos, sin, s["q8"], s["k8"], s["qs"], s["ks"],
-                                             s["qy"], None, eps=wl.eps, fp8_max=wl.fp8_max) for s in sets]
+    if wl.fused_qkv or pos is not None:
+        launches = [rnq.prepare_qk_norm_rope_fp8_ex(s["q"], s["k"], wq, wk, cos, sin, s["q8"], s["k8"], s["qs"],
+                                                    s["ks"], s["qy"], None, positions=pos, eps=wl.eps,
+                                                    fp8_max=wl.fp8_max) for s in sets]
+    else:
+        launches = [rnq.prepare_qk_norm_rope_fp8(s["q"], s["k"], wq, wk, cos, sin, s["q8"], s["k8"], s["qs"],
+                                                 s["ks"], s["qy"], None, eps=wl.eps, fp8_max=wl.fp8_max)
+                    for s in sets]
     ms = _timed(torch, launches, steps, warmup)
     out = {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
     del sets
@@ -121,14 +137,21 @@ def bench_norm_rope(torch, rnq, workloads, ledger, name, steps, warmup):
     d = workloads.generate(name)
     M, N, R = d["rows"], d["width"], d["rope_dim"]
     led = ledger.norm_rope_bytes(M, N, R, d["rows_per_token"])
+    pos_cpu = d.get("positions")
+    if pos_cpu is not None:
+        led = ledger.gathered_table_adjust(led, M // d["rows_per_token"], R, len(set(pos_cpu.tolist())))
     dev = torch.device("cuda:0")
     n_sets = _n_sets(led["total"])
     sets = [{"x": d["x"].to(dev), "y": torch.empty_like(d["x"], device=dev),
              "cos": d["cos"].to(dev), "sin": d["sin"].to(dev)} for _ in range(n_sets)]
     w = d["w"].to(dev)
-
-    launches = [rnq.prepare_rmsnorm_rope(s["x"], w, s["cos"], s["sin"], s["y"], rows_per_token=d["rows_per_token"])
-                for s in sets]
+    if pos_cpu is not None:
+        pos = pos_cpu.to(dev)
+        launches = [rnq.prepare_rmsnorm_rope_ex(s["x"], w, s["cos"], s["sin"], s["y"], positions=pos,
+                                                rows_per_token=d["rows_per_token"]) for s in sets]
+    else:
+        launches = [rnq.prepare_rmsnorm_rope(s["x"], w, s["cos"], s["sin"], s["y"],
+                                             rows_per_token=d["rows_per_token"]) for s in sets]
     ms = _timed(torch, launches, steps, warmup)
     del sets
     torch.cuda.empty_cache()
@@ -343,6 +366,8 @@ def main() -> int:
         paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
         paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
         paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
+        paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_4k_fused", steps, warm)))
+        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 20)))
         out["other_paths"] = paths
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)

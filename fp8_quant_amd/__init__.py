@@ -30,7 +30,11 @@ __all__ = [
     "rnq_rmsnorm_bwd_workspace_size",
     "rnq_rmsnorm_rope_fp8_grouped",
     "rnq_rmsnorm_rope_bwd",
+    "rnq_qk_norm_rope_fp8_ex",
+    "rnq_rmsnorm_rope_ex",
     "prepare_qk_norm_rope_fp8",
+    "prepare_qk_norm_rope_fp8_ex",
+    "prepare_rmsnorm_rope_ex",
     "prepare_rmsnorm_rope_fp8_grouped",
     "prepare_rmsnorm_rope",
     "prepare_rmsnorm_fwd",
@@ -57,6 +61,8 @@ EXPORTED_SYMBOLS = (
     "rnq_qk_norm_rope_fp8",
     "rnq_rmsnorm_rope_fp8_grouped",
     "rnq_rmsnorm_rope_bwd",
+    "rnq_qk_norm_rope_fp8_ex",
+    "rnq_rmsnorm_rope_ex",
 )
 
 RNQ_BF16 = 0
@@ -108,6 +114,11 @@ def load_library():
     lib.rnq_rmsnorm_rope_fp8_grouped.restype = i32
     lib.rnq_rmsnorm_rope_bwd.argtypes = [vp] * 9 + [ctypes.c_size_t] + [i64] * 4 + [f32, i32, vp]
     lib.rnq_rmsnorm_rope_bwd.restype = i32
+    lib.rnq_qk_norm_rope_fp8_ex.argtypes = [vp, i64, vp, i64] + [vp] * 5 + [i64] + [vp] * 6 + [i64] * 5 + [f32, f32,
+                                                                                                       i32, vp]
+    lib.rnq_qk_norm_rope_fp8_ex.restype = i32
+    lib.rnq_rmsnorm_rope_ex.argtypes = [vp, i64] + [vp] * 4 + [i64, vp] + [i64] * 4 + [f32, i32, vp]
+    lib.rnq_rmsnorm_rope_ex.restype = i32
     _lib = lib
     return lib
 
@@ -132,6 +143,36 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _token_view(t, heads: int, width: int, what: str):
+    """Pointer and token stride (elements) of a [T, heads, width] view whose rows of one
+    token are contiguous (a slice of a fused projection output, say); stride 0 when the
+    whole tensor is contiguous."""
+    if t is None:
+        return None, 0
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor on {t.device}: the rnq kernels need GPU tensors (no CPU path)")
+    if t.is_contiguous():
+        return ctypes.c_void_p(t.data_ptr()), 0
+    if t.dim() != 3 or t.stride(2) != 1 or (heads > 1 and t.stride(1) != width):
+        raise ValueError(f"{what}: expected a [T, H, D] view with contiguous rows inside a token "
+                         f"(strides (S, {width}, 1)), got strides {tuple(t.stride())}")
+    return ctypes.c_void_p(t.data_ptr()), int(t.stride(0))
+
+
+def _positions(positions, tokens: int):
+    torch = _torch()
+    if positions is None:
+        return None
+    if positions.dtype != torch.int32:
+        raise TypeError(f"positions: dtype {positions.dtype}, expected torch.int32")
+    if tuple(positions.shape) != (tokens,):
+        raise ValueError(f"positions: shape {tuple(positions.shape)}, expected {(tokens,)}")
+    return _ptr(positions)
 
 
 def _dtype_code(t) -> int:
@@ -224,6 +265,83 @@ def prepare_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_sc
         T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
     )
     return _launcher(lib.rnq_qk_norm_rope_fp8, args)
+
+
+def rnq_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None, *,
+                            positions=None, eps: float = 1e-6, fp8_max: float = 448.0, stream=None) -> None:
+    """rnq_qk_norm_rope_fp8 with q / k as [T, H, D] views (token stride from the view) and
+    cos/sin rows gathered through int32 ``positions`` [T] from a [table_rows, R/2] table."""
+    prepare_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y, k_y,
+                                positions=positions, eps=eps, fp8_max=fp8_max, stream=stream)()
+
+
+def prepare_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None, *,
+                                positions=None, eps: float = 1e-6, fp8_max: float = 448.0, stream=None):
+    torch = _torch()
+    lib = load_library()
+    T, Hq, D = q.shape
+    Hk = 0 if k is None else k.shape[1]
+    half = 0 if cos is None else cos.shape[-1]
+    dt = q.dtype
+    if k is not None and (k.dtype != dt or tuple(k.shape) != (T, Hk, D)):
+        raise ValueError(f"k: expected {dt} of shape {(T, Hk, D)}")
+    _expect(wq, dt, (D,), "wq")
+    _expect(wk, dt, (D,), "wk")
+    table_rows = T if positions is None else (0 if cos is None else cos.shape[0])
+    if cos is not None:
+        _expect(cos, torch.float32, (table_rows, half), "cos")
+        _expect(sin, torch.float32, (table_rows, half), "sin")
+    for o, H, nm in ((q_fp8, Hq, "q_fp8"), (k_fp8, Hk, "k_fp8")):
+        if o is not None and o.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{nm}: expected uint8 or float8_e4m3fn")
+        if o is not None and tuple(o.shape) != (T, H, D):
+            raise ValueError(f"{nm}: shape {tuple(o.shape)}, expected {(T, H, D)}")
+    _expect(q_scale, torch.float32, (T, Hq), "q_scale")
+    _expect(k_scale, torch.float32, (T, Hk), "k_scale")
+    _expect(q_y, dt, (T, Hq, D), "q_y")
+    _expect(k_y, dt, (T, Hk, D), "k_y")
+    qp, qs_ = _token_view(q, Hq, D, "q")
+    kp, ks_ = _token_view(k, Hk, D, "k")
+    args = (
+        qp, qs_, kp, ks_, _ptr(wq), _ptr(wk), _ptr(cos), _ptr(sin), _positions(positions, T), table_rows,
+        _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale), _ptr(k_scale), _ptr(q_y), _ptr(k_y),
+        T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
+    )
+    return _launcher(lib.rnq_qk_norm_rope_fp8_ex, args)
+
+
+def rnq_rmsnorm_rope_ex(x, w, cos, sin, y, *, positions=None, rows_per_token: int = 1, eps: float = 1e-6,
+                        stream=None) -> None:
+    """rnq_rmsnorm_rope with x as a [T, rows_per_token, N] view (or a [M, N] view when
+    rows_per_token is 1) and cos/sin gathered through int32 ``positions`` [T]."""
+    prepare_rmsnorm_rope_ex(x, w, cos, sin, y, positions=positions, rows_per_token=rows_per_token, eps=eps,
+                            stream=stream)()
+
+
+def prepare_rmsnorm_rope_ex(x, w, cos, sin, y, *, positions=None, rows_per_token: int = 1, eps: float = 1e-6,
+                            stream=None):
+    torch = _torch()
+    lib = load_library()
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    r = max(rows_per_token, 1)
+    T = M // r
+    half = 0 if cos is None else cos.shape[-1]
+    _expect(w, x.dtype, (N,), "w")
+    if y is not None and (y.dtype != x.dtype or y.numel() != M * N or not y.is_contiguous()):
+        raise ValueError(f"y: expected a contiguous {x.dtype} tensor of {M} x {N}")
+    table_rows = T if positions is None else (0 if cos is None else cos.shape[0])
+    if cos is not None:
+        _expect(cos, torch.float32, (table_rows, half), "cos")
+        _expect(sin, torch.float32, (table_rows, half), "sin")
+    if x.dim() == 2 and r == 1 and not x.is_contiguous():
+        xv = x.unsqueeze(1)
+    else:
+        xv = x if x.dim() == 3 else x.reshape(T, r, N) if x.is_contiguous() else x
+    xp, xs = _token_view(xv, r, N, "x")
+    args = (xp, xs, _ptr(w), _ptr(cos), _ptr(sin), _positions(positions, T), table_rows, _ptr(y), M, N, 2 * half,
+            rows_per_token, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_rope_ex, args)
 
 
 def rnq_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float = 1e-6, stream=None) -> None:
@@ -341,8 +459,12 @@ def prepare_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, g
 # ------------------------------------------------------- allocating wrappers
 
 
-def qk_norm_rope_fp8(q, k, wq, wk, cos, sin, *, eps=1e-6, fp8_max=448.0, return_y=False):
-    """Returns (q8, k8, q_scale, k_scale[, q_y, k_y]); codes as torch.float8_e4m3fn."""
+def qk_norm_rope_fp8(q, k, wq, wk, cos, sin, *, positions=None, eps=1e-6, fp8_max=448.0, return_y=False):
+    """Returns (q8, k8, q_scale, k_scale[, q_y, k_y]); codes as torch.float8_e4m3fn.
+
+    q / k may be [T, H, D] views with contiguous rows inside a token (slices of a
+    fused QKV output); with int32 ``positions`` [T], cos/sin are a [table_rows, R/2]
+    table indexed by position."""
     torch = _torch()
     T, Hq, D = q.shape
     Hk = 0 if k is None else k.shape[1]
@@ -351,10 +473,15 @@ def qk_norm_rope_fp8(q, k, wq, wk, cos, sin, *, eps=1e-6, fp8_max=448.0, return_
     k8 = torch.empty((T, Hk, D), dtype=torch.uint8, device=dev)
     qs = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     ks = torch.empty((T, Hk), dtype=torch.float32, device=dev)
-    qy = torch.empty_like(q) if return_y else None
-    ky = (torch.empty_like(k) if k is not None else None) if return_y else None
-    rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q8, k8 if Hk else None, qs, ks if Hk else None, qy, ky,
-                         eps=eps, fp8_max=fp8_max)
+    qy = torch.empty((T, Hq, D), dtype=q.dtype, device=dev) if return_y else None
+    ky = (torch.empty((T, Hk, D), dtype=q.dtype, device=dev) if k is not None else None) if return_y else None
+    contiguous = q.is_contiguous() and (k is None or k.is_contiguous())
+    if contiguous and positions is None:
+        rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q8, k8 if Hk else None, qs, ks if Hk else None, qy, ky,
+                             eps=eps, fp8_max=fp8_max)
+    else:
+        rnq_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q8, k8 if Hk else None, qs, ks if Hk else None, qy, ky,
+                                positions=positions, eps=eps, fp8_max=fp8_max)
     out = (q8.view(torch.float8_e4m3fn), k8.view(torch.float8_e4m3fn), qs, ks)
     return out + (qy, ky) if return_y else out
 
@@ -389,10 +516,16 @@ def rmsnorm_rope_bwd(x, w, grad_y, cos, sin, rstd=None, *, rows_per_token=1, eps
     return gx, gw
 
 
-def rmsnorm_rope(x, w, cos, sin, *, rows_per_token=1, eps=1e-6):
+def rmsnorm_rope(x, w, cos, sin, *, rows_per_token=1, positions=None, eps=1e-6):
+    """y [M, N] (contiguous); x may be a strided view, cos/sin gathered through ``positions``."""
     torch = _torch()
-    y = torch.empty_like(x)
-    rnq_rmsnorm_rope(x, w, cos, sin, y, rows_per_token=rows_per_token, eps=eps)
+    if x.is_contiguous() and x.dim() == 2 and positions is None:
+        y = torch.empty_like(x)
+        rnq_rmsnorm_rope(x, w, cos, sin, y, rows_per_token=rows_per_token, eps=eps)
+        return y
+    N = x.shape[-1]
+    y = torch.empty((x.numel() // N, N), dtype=x.dtype, device=x.device)
+    rnq_rmsnorm_rope_ex(x, w, cos, sin, y, positions=positions, rows_per_token=rows_per_token, eps=eps)
     return y
 
 

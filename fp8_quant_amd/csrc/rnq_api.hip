@@ -84,11 +84,16 @@ int rnq_abi_version(void) { return 100; }
 
 // One row-kernel launch over tensor 0 (heads0 heads per token) and tensor 1
 // (heads1 heads per token), rows in token-major order.
-static hipError_t launch_qk(const void* x0, const void* w0, uint8_t* c0, float* s0, void* y0, const void* x1,
-                            const void* w1, uint8_t* c1, float* s1, void* y1, const float* cos, const float* sin,
+static hipError_t launch_qk(const void* x0, int64_t xs0, const void* w0, uint8_t* c0, float* s0, void* y0,
+                            const void* x1, int64_t xs1, const void* w1, uint8_t* c1, float* s1, void* y1,
+                            const float* cos, const float* sin, const int32_t* positions, int64_t table_rows,
                             int64_t tokens, int64_t heads0, int64_t heads1, int64_t head_dim, int64_t rope_dim,
                             float eps, float fp8_max, int dtype, hipStream_t stream) {
   RowParams p = {};
+  p.xs0 = (uint64_t)xs0;
+  p.xs1 = (uint64_t)xs1;
+  p.positions = positions;
+  p.max_pos = (uint32_t)table_rows;
   p.x0 = (const uint16_t*)x0;
   p.w0 = (const uint16_t*)w0;
   p.c0 = c0;
@@ -111,13 +116,35 @@ static hipError_t launch_qk(const void* x0, const void* w0, uint8_t* c0, float* 
   return launch_rows(p, (int)head_dim, dtype == RNQ_BF16, true, stream);
 }
 
-rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, const void* wk,
-                                const float* cos, const float* sin,
-                                uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
-                                void* q_y, void* k_y,
-                                int64_t tokens, int64_t q_heads, int64_t kv_heads,
-                                int64_t head_dim, int64_t rope_dim,
-                                float eps, float fp8_max, int dtype, void* stream) {
+// A token stride (elements between the first rows of consecutive tokens):
+// 0 means contiguous; otherwise at least the token's rows and a multiple of 8
+// (every row 16-byte aligned).
+static rnq_status check_stride(const char* what, int64_t stride, int64_t rows_per_token, int64_t width) {
+  if (stride == 0) return RNQ_OK;
+  if (stride < rows_per_token * width)
+    return fail(RNQ_ERR_SHAPE, "%s token stride %lld is below the token's %lld elements", what, (long long)stride,
+                (long long)(rows_per_token * width));
+  if (stride % 8 != 0)
+    return fail(RNQ_ERR_UNSUPPORTED, "%s token stride %lld is not a multiple of 8 elements", what, (long long)stride);
+  return RNQ_OK;
+}
+
+static rnq_status check_positions(const int32_t* positions, int64_t table_rows, int64_t rope_dim) {
+  if (positions == nullptr || rope_dim == 0) return RNQ_OK;
+  if (table_rows < 1) return fail(RNQ_ERR_SHAPE, "table_rows must be >= 1 when positions are given");
+  if (table_rows >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "table_rows must stay below 2^31");
+  if (!aligned(positions, 4)) return fail(RNQ_ERR_UNSUPPORTED, "positions must be 4-byte aligned");
+  return RNQ_OK;
+}
+
+rnq_status rnq_qk_norm_rope_fp8_ex(const void* q, int64_t q_token_stride, const void* k, int64_t k_token_stride,
+                                   const void* wq, const void* wk, const float* cos, const float* sin,
+                                   const int32_t* positions, int64_t table_rows,
+                                   uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                   void* q_y, void* k_y,
+                                   int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                   int64_t head_dim, int64_t rope_dim,
+                                   float eps, float fp8_max, int dtype, void* stream) {
   rnq_status s;
   if ((s = check_dtype(dtype)) != RNQ_OK) return s;
   if (tokens < 0 || q_heads < 0 || kv_heads < 0 || head_dim < 0)
@@ -125,6 +152,9 @@ rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, co
                 (long long)tokens, (long long)q_heads, (long long)kv_heads, (long long)head_dim);
   if ((s = check_rope(rope_dim, head_dim)) != RNQ_OK) return s;
   if (!row_width_ok(head_dim)) return fail(RNQ_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512 (got %lld)", (long long)head_dim);
+  if ((s = check_stride("q", q_token_stride, q_heads, head_dim)) != RNQ_OK) return s;
+  if ((s = check_stride("k", k_token_stride, kv_heads, head_dim)) != RNQ_OK) return s;
+  if ((s = check_positions(positions, table_rows, rope_dim)) != RNQ_OK) return s;
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
   const int64_t heads = q_heads + kv_heads;
@@ -144,25 +174,40 @@ rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, co
   const hipStream_t st = (hipStream_t)stream;
   if (q_heads > 0 && kv_heads > 0 && (q_y == nullptr) != (k_y == nullptr)) {
     // y for one tensor only: one launch per tensor, so that each launch writes y for all its rows or none
-    hipError_t e = launch_qk(q, wq, q_fp8, q_scale, q_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin,
-                             tokens, q_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+    hipError_t e = launch_qk(q, q_token_stride, wq, q_fp8, q_scale, q_y, nullptr, 0, nullptr, nullptr, nullptr,
+                             nullptr, cos, sin, positions, table_rows, tokens, q_heads, 0, head_dim, rope_dim, eps,
+                             fp8_max, dtype, st);
     if (e == hipSuccess)
-      e = launch_qk(k, wk, k_fp8, k_scale, k_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin,
-                    tokens, kv_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+      e = launch_qk(k, k_token_stride, wk, k_fp8, k_scale, k_y, nullptr, 0, nullptr, nullptr, nullptr, nullptr, cos,
+                    sin, positions, table_rows, tokens, kv_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
     return hip_status(e, "rnq_qk_norm_rope_fp8");
   }
   const bool q_first = q_heads > 0;  // tensor 0 is q unless there are no q heads
   const hipError_t e =
-      q_first ? launch_qk(q, wq, q_fp8, q_scale, q_y, k, wk, k_fp8, k_scale, k_y, cos, sin, tokens, q_heads, kv_heads,
-                          head_dim, rope_dim, eps, fp8_max, dtype, st)
-              : launch_qk(k, wk, k_fp8, k_scale, k_y, nullptr, nullptr, nullptr, nullptr, nullptr, cos, sin, tokens,
-                          kv_heads, 0, head_dim, rope_dim, eps, fp8_max, dtype, st);
+      q_first ? launch_qk(q, q_token_stride, wq, q_fp8, q_scale, q_y, k, k_token_stride, wk, k_fp8, k_scale, k_y, cos,
+                          sin, positions, table_rows, tokens, q_heads, kv_heads, head_dim, rope_dim, eps, fp8_max,
+                          dtype, st)
+              : launch_qk(k, k_token_stride, wk, k_fp8, k_scale, k_y, nullptr, 0, nullptr, nullptr, nullptr, nullptr,
+                          cos, sin, positions, table_rows, tokens, kv_heads, 0, head_dim, rope_dim, eps, fp8_max,
+                          dtype, st);
   return hip_status(e, "rnq_qk_norm_rope_fp8");
 }
 
-rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,
-                            void* y, int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
-                            float eps, int dtype, void* stream) {
+rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, const void* wk,
+                                const float* cos, const float* sin,
+                                uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                void* q_y, void* k_y,
+                                int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, int64_t rope_dim,
+                                float eps, float fp8_max, int dtype, void* stream) {
+  return rnq_qk_norm_rope_fp8_ex(q, 0, k, 0, wq, wk, cos, sin, nullptr, 0, q_fp8, k_fp8, q_scale, k_scale, q_y, k_y,
+                                 tokens, q_heads, kv_heads, head_dim, rope_dim, eps, fp8_max, dtype, stream);
+}
+
+rnq_status rnq_rmsnorm_rope_ex(const void* x, int64_t x_token_stride, const void* w, const float* cos,
+                               const float* sin, const int32_t* positions, int64_t table_rows, void* y, int64_t M,
+                               int64_t N, int64_t rope_dim, int64_t rows_per_token, float eps, int dtype,
+                               void* stream) {
   rnq_status s;
   if ((s = check_dtype(dtype)) != RNQ_OK) return s;
   if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
@@ -170,6 +215,8 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
   if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
   if (M % rows_per_token != 0) return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
   if (!row_width_ok(N)) return fail(RNQ_ERR_UNSUPPORTED, "N must be 64, 128, 256 or 512 (got %lld)", (long long)N);
+  if ((s = check_stride("x", x_token_stride, rows_per_token, N)) != RNQ_OK) return s;
+  if ((s = check_positions(positions, table_rows, rope_dim)) != RNQ_OK) return s;
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
   if (M == 0) return ok();
@@ -181,10 +228,13 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
 
   RowParams p = {};
   p.x0 = (const uint16_t*)x;
+  p.xs0 = (uint64_t)x_token_stride;
   p.w0 = (const uint16_t*)w;
   p.y0 = (uint16_t*)y;
   p.cos = cos;
   p.sin = sin;
+  p.positions = positions;
+  p.max_pos = (uint32_t)table_rows;
   p.total_rows = (uint32_t)M;
   p.heads = (uint32_t)rows_per_token;
   p.heads0 = (uint32_t)rows_per_token;
@@ -192,6 +242,12 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
   p.eps = eps;
   p.fp8_max = 448.0f;
   return hip_status(launch_rows(p, (int)N, dtype == RNQ_BF16, false, (hipStream_t)stream), "rnq_rmsnorm_rope");
+}
+
+rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,
+                            void* y, int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
+                            float eps, int dtype, void* stream) {
+  return rnq_rmsnorm_rope_ex(x, 0, w, cos, sin, nullptr, 0, y, M, N, rope_dim, rows_per_token, eps, dtype, stream);
 }
 
 rnq_status rnq_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out,

@@ -15,8 +15,12 @@ struct RowParams {
   const uint16_t* x1;
   const uint16_t* w0;
   const uint16_t* w1;
-  const float* cos;  // [tokens, rope/2]
+  const float* cos;  // [tokens, rope/2], or [max_pos, rope/2] gathered through positions
   const float* sin;
+  const int32_t* positions;  // optional [tokens]: table row of each token (ROW_POS)
+  uint64_t xs0;  // token strides of x0 / x1 in elements (rows of a token are contiguous)
+  uint64_t xs1;
+  uint32_t max_pos;  // table rows when positions are given (positions are clamped into range)
   uint8_t* c0;  // codes (quantising kernels)
   uint8_t* c1;
   float* s0;    // scales
@@ -48,6 +52,7 @@ enum RowMode : int {
   ROW_ROPE = 2,   // rotate the rope tail
   ROW_Y = 4,      // write y (16-bit)
   ROW_RSTD = 8,   // write per-row rstd
+  ROW_POS = 16,   // table row of token t is positions[t]
 };
 
 hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStream_t stream);

@@ -28,6 +28,11 @@
 //    both multiples of G, the usual QK layout), a pass's token and tensor are
 //    wave-uniform and its addresses are one scalar base plus lane-constant
 //    offsets. Otherwise each lane locates its own row.
+//  * Inputs may be views: the rows of a token are contiguous in each input
+//    tensor, and consecutive tokens are xs0 / xs1 elements apart (q and k
+//    inside a fused QKV projection output). Outputs are contiguous.
+//  * The cos/sin row of token t is row t, or row positions[t] of a
+//    position-indexed table (clamped into it), gathered as it is read.
 //  * The two weight vectors are staged once per workgroup in LDS (fp32).
 //  * Row sums: sum of squares in fp64 (exact for 16-bit inputs) and the
 //    absmax, each reduced over the L lanes with DPP.
@@ -67,8 +72,10 @@ struct Opts {
 struct Loc {
   uint32_t row;   // flattened (token, head) index (clamped into range)
   uint32_t tok;
+  uint32_t trow;  // cos/sin table row (the token, or its position)
   uint32_t ri;    // row index inside its tensor
   uint32_t ri0;   // aligned passes: row index of the pass's first row (wave-uniform)
+  uint64_t xoff;  // element offset of the input row (aligned passes: of the pass's first row)
   bool second;    // row of tensor 1 (k)
 };
 
@@ -86,7 +93,7 @@ __device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) 
   return (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);  // row / heads, exact below 2^31
 }
 
-template <int G, bool ALIGNED>
+template <int G, int D, bool ALIGNED, bool POS>
 __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_t slot) {
   Loc r;
   if constexpr (ALIGNED) {
@@ -98,12 +105,13 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
     const uint32_t t = __builtin_amdgcn_readfirstlane(div_heads(p, row0));
     const uint32_t h0 = row0 - t * p.heads;
     r.second = h0 >= p.heads0;
-    const uint32_t ri0 = __builtin_amdgcn_readfirstlane(
-        r.second ? t * (p.heads - p.heads0) + (h0 - p.heads0) : t * p.heads0 + h0);
+    const uint32_t hk = __builtin_amdgcn_readfirstlane(r.second ? h0 - p.heads0 : h0);  // head inside its tensor
+    const uint32_t ri0 = __builtin_amdgcn_readfirstlane(r.second ? t * (p.heads - p.heads0) + hk : t * p.heads0 + hk);
     r.tok = t;
     r.ri0 = ri0;
     r.ri = ri0 + slot;
     r.row = row0 + slot;
+    r.xoff = (uint64_t)t * (r.second ? p.xs1 : p.xs0) + (uint64_t)hk * D;
   } else {
     // rows past the end repeat the last row (same inputs, same bytes written)
     const uint32_t row = min(pass * (uint32_t)G + slot, p.total_rows - 1);
@@ -112,8 +120,16 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
     const uint32_t h = row - t * p.heads;
     r.tok = t;
     r.second = h >= p.heads0;
-    r.ri = r.second ? t * (p.heads - p.heads0) + (h - p.heads0) : t * p.heads0 + h;
+    const uint32_t hk = r.second ? h - p.heads0 : h;
+    r.ri = r.second ? t * (p.heads - p.heads0) + hk : t * p.heads0 + hk;
     r.ri0 = 0;
+    r.xoff = (uint64_t)t * (r.second ? p.xs1 : p.xs0) + (uint64_t)hk * D;
+  }
+  r.trow = r.tok;
+  if constexpr (POS) {
+    // positions outside [0, max_pos) read the last table row (never out of range)
+    r.trow = min((uint32_t)p.positions[r.tok], p.max_pos - 1);
+    if constexpr (ALIGNED) r.trow = __builtin_amdgcn_readfirstlane(r.trow);
   }
   return r;
 }
@@ -124,6 +140,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr bool ROPE = (MODE & ROW_ROPE) != 0;
   constexpr bool WY = (MODE & ROW_Y) != 0;
   constexpr bool WR = (MODE & ROW_RSTD) != 0;
+  constexpr bool POS = (MODE & ROW_POS) != 0;
   constexpr int D = 16 * L;
   constexpr int G = 64 / L;
   __shared__ float w_lds[2 * D];
@@ -175,14 +192,14 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   float* t_wave = t_lds + (STAGED ? wave * D : 0);
 
   auto load_data = [&](Data& d, uint32_t pass) {
-    d.loc = locate<G, ALIGNED>(p, pass, slot);
+    d.loc = locate<G, D, ALIGNED, POS>(p, pass, slot);
     if constexpr (ALIGNED) {
       // the pass's G rows: one wave-uniform descriptor, lane byte offsets
-      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri0 * D, 2u * G * D);
+      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, 2u * G * D);
       d.xa = buf_load16_nt(rx, 2u * pe_a);
       d.xb = buf_load16_nt(rx, 2u * pe_b);
     } else {
-      const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + (size_t)d.loc.ri * D;
+      const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + d.loc.xoff;
       d.xa = load_stream16(src + off_a);
       d.xb = load_stream16(src + off_b);
     }
@@ -193,13 +210,13 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       if constexpr (ALIGNED) {
         // the token's cos and sin rows (wave-uniform descriptors), one chunk
         // of each per lane; the rows go through LDS to the lanes that use them
-        const rsrc_t rc = make_rsrc(p.cos + (size_t)r.tok * half, 4u * half);
-        const rsrc_t rs = make_rsrc(p.sin + (size_t)r.tok * half, 4u * half);
+        const rsrc_t rc = make_rsrc(p.cos + (size_t)r.trow * half, 4u * half);
+        const rsrc_t rs = make_rsrc(p.sin + (size_t)r.trow * half, 4u * half);
         t.cw = buf_load16(rc, tq);
         t.sw = buf_load16(rs, tq);
       } else {
-        const float* cp = p.cos + (size_t)r.tok * half + cs_off;
-        const float* sp = p.sin + (size_t)r.tok * half + cs_off;
+        const float* cp = p.cos + (size_t)r.trow * half + cs_off;
+        const float* sp = p.sin + (size_t)r.trow * half + cs_off;
         t.c0 = *(const float4*)cp;
         t.c1 = *(const float4*)(cp + 4);
         t.s0 = *(const float4*)sp;

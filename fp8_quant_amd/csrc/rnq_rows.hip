@@ -39,8 +39,12 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.scale_floor = 1e-4f / p.fp8_max;
   p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;
   p.clamp = quant && fp8_clamp_needed(p.fp8_max) ? 1u : 0u;
+  // contiguous inputs unless the caller gave token strides
+  if (p.xs0 == 0) p.xs0 = (uint64_t)p.heads0 * (uint64_t)head_dim;
+  if (p.xs1 == 0) p.xs1 = (uint64_t)(p.heads - p.heads0) * (uint64_t)head_dim;
+  const bool pos = p.rope > 0 && p.positions != nullptr;
   const int mode = (quant ? ROW_QUANT : 0) | (p.rope > 0 ? ROW_ROPE : 0) | (p.y0 != nullptr ? ROW_Y : 0) |
-                   (p.rstd != nullptr ? ROW_RSTD : 0);
+                   (p.rstd != nullptr ? ROW_RSTD : 0) | (pos ? ROW_POS : 0);
   switch (mode) {
     case ROW_QUANT: return launch_rows_mode<ROW_QUANT>(p, head_dim, bf16, aligned, grid, stream);
     case ROW_QUANT | ROW_ROPE: return launch_rows_mode<ROW_QUANT | ROW_ROPE>(p, head_dim, bf16, aligned, grid, stream);
@@ -50,6 +54,12 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
     case ROW_Y: return launch_rows_mode<ROW_Y>(p, head_dim, bf16, aligned, grid, stream);
     case ROW_Y | ROW_ROPE: return launch_rows_mode<ROW_Y | ROW_ROPE>(p, head_dim, bf16, aligned, grid, stream);
     case ROW_Y | ROW_RSTD: return launch_rows_mode<ROW_Y | ROW_RSTD>(p, head_dim, bf16, aligned, grid, stream);
+    case ROW_QUANT | ROW_ROPE | ROW_POS:
+      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
+    case ROW_QUANT | ROW_ROPE | ROW_Y | ROW_POS:
+      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
+    case ROW_Y | ROW_ROPE | ROW_POS:
+      return launch_rows_mode<ROW_Y | ROW_ROPE | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
     default: return hipErrorInvalidValue;  // not a combination the entry points produce
   }
 }

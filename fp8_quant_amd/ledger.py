@@ -269,6 +269,17 @@ def qk_bytes(tokens, q_heads, kv_heads, head_dim, rope_dim, in_bytes=2, write_y=
     return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
 
 
+def gathered_table_adjust(led: dict, tokens: int, rope_dim: int, unique_rows: int) -> dict:
+    """Bytes of a call whose cos/sin rows are gathered through an int32 positions index:
+    the per-token table term of ``led`` replaced by the distinct table rows touched (each
+    read once) plus the 4-byte positions."""
+    per_token = 2 * tokens * (rope_dim // 2) * 4
+    reads = led["reads"] - per_token + 2 * unique_rows * (rope_dim // 2) * 4 + 4 * tokens
+    out = dict(led, reads=reads)
+    out["total"] = reads + led["writes"]
+    return out
+
+
 def qk_flops(tokens, q_heads, kv_heads, head_dim, rope_dim) -> int:
     """Chapter-28 rule with the RoPE term over rope_dim/2 pairs."""
     rows = tokens * (q_heads + kv_heads)

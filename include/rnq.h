@@ -122,6 +122,19 @@ rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, cons
                             float eps, int dtype, void* stream);
 
 /*
+ * rnq_rmsnorm_rope on a strided, position-indexed input: x_token_stride
+ * elements between the first rows of consecutive tokens (each token's
+ * rows_per_token rows contiguous; 0 = contiguous), and token t (rows
+ * t*rows_per_token ..) uses row positions[t] of cos/sin [table_rows, R/2]
+ * when positions (int32 [M / rows_per_token]) is given, with the clamping and
+ * stride rules of rnq_qk_norm_rope_fp8_ex. y is contiguous [M, N].
+ */
+rnq_status rnq_rmsnorm_rope_ex(const void* x, int64_t x_token_stride, const void* w, const float* cos,
+                               const float* sin, const int32_t* positions, int64_t table_rows, void* y, int64_t M,
+                               int64_t N, int64_t rope_dim, int64_t rows_per_token, float eps, int dtype,
+                               void* stream);
+
+/*
  * Backward of rnq_rmsnorm_rope (the rotation of the chapter 13 fusion page
  * followed back, then the chapter 17 RMSNorm backward). The two casts to
  * `dtype` in the forward count as identities. On the last R = rope_dim
@@ -190,6 +203,32 @@ rnq_status rnq_qk_norm_rope_fp8(const void* q, const void* k, const void* wq, co
                                 int64_t tokens, int64_t q_heads, int64_t kv_heads,
                                 int64_t head_dim, int64_t rope_dim,
                                 float eps, float fp8_max, int dtype, void* stream);
+
+/*
+ * rnq_qk_norm_rope_fp8 on strided, position-indexed inputs (the chapter 28
+ * page's prologue reads q and k straight from the projection output and
+ * looks the rotation up by token position; chapter 13 fusion page, the
+ * [tokens, rope_dim/2] cos/sin layout):
+ *   * q_token_stride / k_token_stride: elements between the first rows of
+ *     consecutive tokens; the Hq (Hk) rows of a token are contiguous. 0 means
+ *     contiguous (Hq*D, Hk*D). Otherwise at least Hq*D (Hk*D) (SHAPE) and a
+ *     multiple of 8 (UNSUPPORTED), e.g. q and k as views into a fused QKV
+ *     output [T, (Hq + 2*Hk) * D].
+ *   * positions: optional int32 [T] (4-byte aligned). When given, token t uses
+ *     row positions[t] of cos/sin [table_rows, R/2]; a position outside
+ *     [0, table_rows) reads row table_rows - 1 (nothing is read out of range).
+ *     When NULL, cos/sin are [T, R/2] and table_rows is ignored.
+ * Everything else (outputs contiguous) is as rnq_qk_norm_rope_fp8, which is
+ * this call with strides 0 and no positions.
+ */
+rnq_status rnq_qk_norm_rope_fp8_ex(const void* q, int64_t q_token_stride, const void* k, int64_t k_token_stride,
+                                   const void* wq, const void* wk, const float* cos, const float* sin,
+                                   const int32_t* positions, int64_t table_rows,
+                                   uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                   void* q_y, void* k_y,
+                                   int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                   int64_t head_dim, int64_t rope_dim,
+                                   float eps, float fp8_max, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

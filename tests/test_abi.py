@@ -184,3 +184,31 @@ def test_autograd_refuses_cpu_tensors():
     cos = torch.ones(4, 32)
     with pytest.raises(ValueError, match="GPU"):
         rag.rmsnorm_rope(x, w, cos, torch.zeros(4, 32))
+
+
+def test_strided_entry_validation():
+    lib = _lib()
+    P = ctypes.c_void_p(0x20000)  # positions (never dereferenced)
+
+    def qk(qs=0, ks=0, pos=None, rows=64, T=64, Hq=32, Hk=8, D=128, R=128):
+        return lib.rnq_qk_norm_rope_fp8_ex(FAKE, qs, FAKE, ks, FAKE, FAKE, FAKE, FAKE, pos, rows, FAKE, FAKE,
+                                           FAKE, FAKE, None, None, T, Hq, Hk, D, R, 1e-6, 448.0, 0, None)
+
+    assert qk(qs=32 * 128 - 8) == 2  # below the token's rows
+    assert qk(qs=48 * 128 + 4) == 3  # not a multiple of 8 elements
+    assert qk(ks=8 * 128 - 8) == 2
+    assert qk(pos=P, rows=0) == 2  # positions need a table
+    assert qk(pos=ctypes.c_void_p(0x20002)) == 3  # positions misaligned
+    assert qk(T=0) == 0
+    assert lib.rnq_qk_norm_rope_fp8_ex(None, 0, None, 0, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, None, FAKE, None,
+                                       None, None, 4, 1, 0, 128, 64, 1e-6, 448.0, 0, None) == 1
+
+    def nr(xs=0, pos=None, rows=16, M=64, N=128, R=64, rpt=4):
+        return lib.rnq_rmsnorm_rope_ex(FAKE, xs, FAKE, FAKE, FAKE, pos, rows, FAKE, M, N, R, rpt, 1e-6, 0, None)
+
+    assert nr(xs=4 * 128 - 8) == 2
+    assert nr(xs=4 * 128 + 12) == 3
+    assert nr(pos=P, rows=-1) == 2
+    assert nr(M=62) == 2
+    assert nr(N=1024) == 3
+    assert nr(M=0) == 0

@@ -17,6 +17,12 @@ where M = tokens x heads, weight ``[N]``, cos/sin ``[tokens, rope_dim/2]``):
 * ``grouped_small`` - 256 rows x 4096, rope 128, fp16, one scale per 128 elements
   (the shape of the fusion page's own check of its per-group kernel)
 * ``grouped_4k`` - 4096 rows x 4096, rope 128, bf16, one scale per 128 elements, y written
+* ``qk_4k_fused`` - ``qk_4k``'s shapes read from a fused QKV projection output
+  [4096, (32 + 2*8) * 128] (q and k are strided views), cos/sin gathered through
+  positions (8 packed sequences, positions restart at 0 in each) from a
+  [4096, 64] table
+* ``norm_rope_pos`` - ``norm_rope_fp16``'s shapes with cos/sin gathered through
+  the random positions from a [8192, 32] table instead of one table row per row
 """
 
 from __future__ import annotations
@@ -59,6 +65,8 @@ class Workload:
     x_std: float = 1.0
     positions: str = "index"  # "index" (pos = token/row index) or "random:<hi>"
     group_size: int = 0  # grouped: elements per scale
+    cache_rows: int = 0  # > 0: cos/sin are a [cache_rows, R/2] table indexed through positions
+    fused_qkv: bool = False  # qk: q and k are views into one [T, (Hq + 2 Hk) * D] buffer
     description: str = ""
 
 
@@ -99,6 +107,18 @@ WORKLOADS: dict[str, Workload] = {
             write_y=True,
             description="RMSNorm + RoPE + per-group FP8, 4096 x 4096, rope 128, bf16, groups of 128, y written",
         ),
+        Workload(
+            "qk_4k_fused", "qk", seed=1008, tokens=4096, q_heads=32, kv_heads=8, head_dim=128,
+            rope_dim=128, outlier_p=0.01, positions="segments:8", cache_rows=4096, fused_qkv=True,
+            description="QK-norm + RoPE + FP8 on q/k views of a fused QKV output, 4096 tokens x (32+8) heads "
+                        "x 128, positions of 8 packed sequences into a 4096-row cos/sin table",
+        ),
+        Workload(
+            "norm_rope_pos", "norm_rope", seed=1009, rows=16384, width=128, rope_dim=64,
+            dtype="fp16", x_std=2.0, positions="random:8192", cache_rows=8192,
+            description="RMSNorm + partial RoPE, 16384 x 128, rope 64, fp16, cos/sin gathered by position "
+                        "from an 8192-row table",
+        ),
     ]
 }
 
@@ -126,9 +146,25 @@ def rope_table(positions: np.ndarray, rope_dim: int, theta: float) -> tuple[np.n
 def _positions(spec: str, n: int, g: torch.Generator) -> np.ndarray:
     if spec == "index":
         return np.arange(n, dtype=np.int64)
-    kind, hi = spec.split(":")
-    assert kind == "random"
-    return torch.randint(0, int(hi), (n,), generator=g).numpy().astype(np.int64)
+    kind, arg = spec.split(":")
+    if kind == "random":
+        return torch.randint(0, int(arg), (n,), generator=g).numpy().astype(np.int64)
+    assert kind == "segments"
+    # int(arg) packed sequences of random lengths; positions restart at 0 in each
+    cuts = np.sort(torch.randperm(max(n - 1, 1), generator=g)[: int(arg) - 1].numpy() + 1) if n > 1 else []
+    starts = np.concatenate([[0], cuts]).astype(np.int64)
+    idx = np.arange(n, dtype=np.int64)
+    return idx - starts[np.searchsorted(starts, idx, side="right") - 1]
+
+
+def _tables(wl: "Workload", pos: np.ndarray, out: dict) -> None:
+    """cos/sin per token, or a position-indexed table plus the int32 positions."""
+    if wl.cache_rows:
+        cos, sin = rope_table(np.arange(wl.cache_rows), wl.rope_dim, wl.theta)
+        out["positions"] = torch.from_numpy(pos.astype(np.int32))
+    else:
+        cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
+    out["cos"], out["sin"] = torch.from_numpy(cos), torch.from_numpy(sin)
 
 
 def _normal(shape, g, std=1.0):
@@ -161,21 +197,24 @@ def generate(name_or_wl, *, tokens: int | None = None, seed: int | None = None) 
         wq = 1.0 + 0.1 * _normal((D,), g)
         wk = 1.0 + 0.1 * _normal((D,), g)
         pos = _positions(wl.positions, T, g)
-        cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
+        _tables(wl, pos, out)
         out.update(
             q=q.to(dt), k=k.to(dt), wq=wq.to(dt), wk=wk.to(dt),
-            cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
             tokens=T, q_heads=Hq, kv_heads=Hk, head_dim=D, rope_dim=wl.rope_dim,
         )
+        if wl.fused_qkv:
+            # [T, (Hq + 2 Hk) * D]: q heads, k heads, then v heads (v is not read)
+            v = _normal((T, Hk, D), g)
+            out["qkv"] = torch.cat([out["q"].reshape(T, -1), out["k"].reshape(T, -1), v.to(dt).reshape(T, -1)], 1)
     elif wl.kind in ("norm_rope", "grouped"):
         M = wl.rows if tokens is None else tokens
         N = wl.width
         x = _normal((M, N), g, wl.x_std)
         w = 1.0 + 0.1 * _normal((N,), g)
         pos = _positions(wl.positions, M, g)
-        cos, sin = rope_table(pos, wl.rope_dim, wl.theta)
+        _tables(wl, pos, out)
         out.update(
-            x=x.to(dt), w=w.to(dt), cos=torch.from_numpy(cos), sin=torch.from_numpy(sin),
+            x=x.to(dt), w=w.to(dt),
             rows=M, width=N, rope_dim=wl.rope_dim, rows_per_token=1, group_size=wl.group_size,
         )
     elif wl.kind == "rmsnorm":
