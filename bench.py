@@ -180,6 +180,68 @@ def bench_grouped(torch, rnq, workloads, ledger, name, steps, warmup):
     return {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
 
 
+def bench_fusion(torch, rnq, workloads, ledger, steps, warmup):
+    """The chapter 13 ledger page's norm+rope+quant plan on nrq_4k: fused (one kernel,
+    one FP8 scale per row) against the three-kernel plan; and the chapter 28 designs
+    A / B / C (1, 8, 40 rows per workgroup) on qk_4k against the row kernel."""
+    from fp8_quant_amd import baselines
+
+    wl = workloads.WORKLOADS["nrq_4k"]
+    d = workloads.generate("nrq_4k")
+    M, N, R = d["rows"], d["width"], d["rope_dim"]
+    fused_b = ledger.norm_rope_quant_bytes(M, N, R)
+    unfused_b = ledger.norm_rope_quant_bytes(M, N, R, unfused=True)
+    dev = torch.device("cuda:0")
+    n_sets = _n_sets(unfused_b["total"])
+    sets = [{"x": d["x"].to(dev), "codes": torch.empty((M, N), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((M, 1), dtype=torch.float32, device=dev),
+             "normed": torch.empty_like(d["x"], device=dev), "rotated": torch.empty_like(d["x"], device=dev)}
+            for _ in range(n_sets)]
+    w, cos, sin = d["w"].to(dev), d["cos"].to(dev), d["sin"].to(dev)
+    fused = [rnq.prepare_rmsnorm_rope_fp8_grouped(s["x"], w, cos, sin, s["codes"], s["scales"], None, group_size=N,
+                                                  eps=wl.eps, fp8_max=wl.fp8_max) for s in sets]
+    unfused = [baselines.prepare_norm_rope_quant_unfused(s["x"], w, cos, sin, s["normed"], s["rotated"], s["codes"],
+                                                         s["scales"].view(M), eps=wl.eps, fp8_max=wl.fp8_max)
+               for s in sets]
+    ms_f = _timed(torch, fused, steps, warmup)
+    ms_u = _timed(torch, unfused, steps, warmup)
+    del sets, fused, unfused
+    torch.cuda.empty_cache()
+    paths = [
+        {"workload": "nrq_4k fused (1 kernel)", "ms": ms_f, "bytes": fused_b["total"], "rows": M, "sets": n_sets},
+        {"workload": "nrq_4k unfused (3 kernels)", "ms": ms_u, "bytes": unfused_b["total"], "rows": M,
+         "sets": n_sets},
+    ]
+    summary = {"plan": "norm+rope+quant 4096x4096 bf16, rope 128, per-row scale",
+               "fused_us": round(ms_f * 1e3, 3), "unfused_us": round(ms_u * 1e3, 3),
+               "measured_time_ratio": round(ms_u / ms_f, 3),
+               "ledger_bytes_ratio": round(unfused_b["total"] / fused_b["total"], 3)}
+
+    # designs A / B / C at the qk_4k shape (outputs equal the row kernel's)
+    dq = workloads.generate("qk_4k")
+    T, Hq, Hk, D, Rq = dq["tokens"], dq["q_heads"], dq["kv_heads"], dq["head_dim"], dq["rope_dim"]
+    led = ledger.qk_bytes(T, Hq, Hk, D, Rq)
+    n_sets = _n_sets(led["total"])
+    qsets = [{"q": dq["q"].to(dev), "k": dq["k"].to(dev),
+              "q8": torch.empty((T, Hq, D), dtype=torch.uint8, device=dev),
+              "k8": torch.empty((T, Hk, D), dtype=torch.uint8, device=dev),
+              "qs": torch.empty((T, Hq), dtype=torch.float32, device=dev),
+              "ks": torch.empty((T, Hk), dtype=torch.float32, device=dev)} for _ in range(n_sets)]
+    wq, wk, qc, qsn = dq["wq"].to(dev), dq["wk"].to(dev), dq["cos"].to(dev), dq["sin"].to(dev)
+    designs = {}
+    for label, rpb in (("A", 1), ("B", 8), ("C", Hq + Hk)):
+        launches = [baselines.prepare_qk_design(s["q"], s["k"], wq, wk, qc, qsn, s["q8"], s["k8"], s["qs"], s["ks"],
+                                                rows_per_block=rpb) for s in qsets]
+        ms = _timed(torch, launches, steps, warmup)
+        designs[label] = round(ms * 1e3, 3)
+        paths.append({"workload": f"qk_4k design {label} ({rpb} rows per workgroup)", "ms": ms,
+                      "bytes": led["total"], "rows": led["rows"], "sets": n_sets})
+    del qsets
+    torch.cuda.empty_cache()
+    summary["qk_4k_designs_us"] = designs
+    return paths, summary
+
+
 def bench_rope_bwd(torch, rnq, workloads, ledger, name, steps, warmup):
     d = workloads.generate(name)
     M, N, R, rpt = d["rows"], d["width"], d["rope_dim"], d["rows_per_token"]
@@ -286,6 +348,8 @@ def main() -> int:
     ap.add_argument("--workload", default="qk_4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-paths", action="store_true", help="time only the headline workload")
+    ap.add_argument("--fusion-only", action="store_true",
+                    help="time only the fused / unfused plan and the designs A/B/C; print their summary")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 256 MiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -321,6 +385,10 @@ def main() -> int:
     # every launch and event goes to one created stream (default priority): the
     # legacy null stream adds about a microsecond of synchronisation per launch
     torch.cuda.set_stream(torch.cuda.Stream(device=0))
+    if args.fusion_only:
+        fpaths, fsum = bench_fusion(torch, rnq, workloads, ledger, args.steps, args.warmup)
+        print(json.dumps({"fusion": fsum, "paths": [_summary(r) for r in fpaths]}), flush=True)
+        return 0
     head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup)
     wl = workloads.WORKLOADS[args.workload]
     ms = head["ms"]
@@ -368,6 +436,9 @@ def main() -> int:
         paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_4k_fused", steps, warm)))
         paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos", steps, warm)))
+        fpaths, fsum = bench_fusion(torch, rnq, workloads, ledger, steps, warm)
+        paths += [_summary(r) for r in fpaths]
+        out["fusion"] = fsum
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 20)))
         out["other_paths"] = paths
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)

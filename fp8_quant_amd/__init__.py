@@ -63,6 +63,8 @@ EXPORTED_SYMBOLS = (
     "rnq_rmsnorm_rope_bwd",
     "rnq_qk_norm_rope_fp8_ex",
     "rnq_rmsnorm_rope_ex",
+    "rnq_baseline_norm_rope_quant_unfused",
+    "rnq_baseline_qk_design",
 )
 
 RNQ_BF16 = 0
@@ -119,6 +121,10 @@ def load_library():
     lib.rnq_qk_norm_rope_fp8_ex.restype = i32
     lib.rnq_rmsnorm_rope_ex.argtypes = [vp, i64] + [vp] * 4 + [i64, vp] + [i64] * 4 + [f32, i32, vp]
     lib.rnq_rmsnorm_rope_ex.restype = i32
+    lib.rnq_baseline_norm_rope_quant_unfused.argtypes = [vp] * 8 + [i64] * 4 + [f32, f32, i32, vp]
+    lib.rnq_baseline_norm_rope_quant_unfused.restype = i32
+    lib.rnq_baseline_qk_design.argtypes = [vp] * 10 + [i64] * 6 + [f32, f32, i32, vp]
+    lib.rnq_baseline_qk_design.restype = i32
     _lib = lib
     return lib
 

@@ -1,5 +1,6 @@
 // C ABI of librnq.so: argument validation and dispatch to the HIP kernels.
-// The contract of every entry point is documented in include/rnq.h.
+// The contract of every entry point is documented in include/rnq.h (the
+// measurement baselines in include/rnq_baselines.h).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -9,6 +10,7 @@
 #include <string>
 
 #include "rnq.h"
+#include "rnq_baselines.h"
 #include "rnq_launch.h"
 
 namespace rnq {
@@ -304,8 +306,8 @@ rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const floa
     return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
   if (group_size <= 0 || (N > 0 && N % group_size != 0))
     return fail(RNQ_ERR_SHAPE, "group_size must divide N (N %lld, group_size %lld)", (long long)N, (long long)group_size);
-  if (group_size < 8 || group_size > 512 || (group_size & (group_size - 1)) != 0)
-    return fail(RNQ_ERR_UNSUPPORTED, "group_size must be a power of two in [8, 512] (got %lld)", (long long)group_size);
+  if (group_size != N && (group_size < 8 || group_size > 512 || (group_size & (group_size - 1)) != 0))
+    return fail(RNQ_ERR_UNSUPPORTED, "group_size must be N or a power of two in [8, 512] (got %lld)", (long long)group_size);
   if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
@@ -419,6 +421,87 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
                                 int64_t rows_per_token, float eps, int dtype, void* stream) {
   return rmsnorm_bwd_common("rnq_rmsnorm_rope_bwd", x, w, grad_y, cos, sin, rstd, grad_x, grad_w, workspace,
                             workspace_bytes, M, N, rope_dim, rows_per_token, eps, dtype, stream);
+}
+
+// ------------------------------------------------------ measurement baselines
+
+rnq_status rnq_baseline_norm_rope_quant_unfused(const void* x, const void* w, const float* cos, const float* sin,
+                                                void* normed, void* rotated, uint8_t* codes, float* scales,
+                                                int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
+                                                float eps, float fp8_max, int dtype, void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
+  if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
+  if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
+  if (M % rows_per_token != 0) return fail(RNQ_ERR_SHAPE, "M is not a multiple of rows_per_token");
+  if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
+  if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !normed || !rotated || !codes || !scales) return fail(RNQ_ERR_NULL, "x, w, normed, rotated, codes and scales are required");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
+  const void* a16[] = {x, w, normed, rotated, cos, sin};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(codes, 8) || !aligned(scales, 4)) return fail(RNQ_ERR_UNSUPPORTED, "codes 8-byte, scales 4-byte aligned");
+  // step 1: the library's RMSNorm forward
+  if ((s = rnq_rmsnorm_fwd(x, w, normed, nullptr, M, N, eps, dtype, stream)) != RNQ_OK) return s;
+  // steps 2 and 3
+  return hip_status(launch_unfused_rope_quant((const uint16_t*)normed, cos, sin, (uint16_t*)rotated, codes, scales,
+                                              (uint32_t)M, (uint32_t)N, (uint32_t)rope_dim, (uint32_t)rows_per_token,
+                                              fp8_max, dtype == RNQ_BF16, (hipStream_t)stream),
+                    "rnq_baseline_norm_rope_quant_unfused");
+}
+
+rnq_status rnq_baseline_qk_design(const void* q, const void* k, const void* wq, const void* wk, const float* cos,
+                                  const float* sin, uint8_t* q_fp8, uint8_t* k_fp8, float* q_scale, float* k_scale,
+                                  int64_t tokens, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
+                                  int64_t rope_dim, int64_t rows_per_block, float eps, float fp8_max, int dtype,
+                                  void* stream) {
+  rnq_status s;
+  if ((s = check_dtype(dtype)) != RNQ_OK) return s;
+  if (tokens < 0 || q_heads < 0 || kv_heads < 0 || head_dim < 0) return fail(RNQ_ERR_SHAPE, "negative size");
+  if ((s = check_rope(rope_dim, head_dim)) != RNQ_OK) return s;
+  if (!row_width_ok(head_dim)) return fail(RNQ_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512 (got %lld)", (long long)head_dim);
+  const int64_t heads = q_heads + kv_heads;
+  if (rows_per_block < 1 || heads % rows_per_block != 0)
+    return fail(RNQ_ERR_SHAPE, "rows_per_block (%lld) must divide the heads per token (%lld)", (long long)rows_per_block, (long long)heads);
+  if (rows_per_block * (head_dim / 8) > 1024)
+    return fail(RNQ_ERR_UNSUPPORTED, "rows_per_block * head_dim / 8 must be at most 1024 threads");
+  if ((s = check_eps(eps)) != RNQ_OK) return s;
+  if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
+  if (heads > 0 && tokens > ((int64_t)1 << 31) / heads) return fail(RNQ_ERR_UNSUPPORTED, "tokens * heads must stay below 2^31");
+  if (tokens * heads == 0) return ok();
+  if (q_heads > 0 && (!q || !wq || !q_fp8 || !q_scale)) return fail(RNQ_ERR_NULL, "q, wq, q_fp8 and q_scale are required");
+  if (kv_heads > 0 && (!k || !wk || !k_fp8 || !k_scale)) return fail(RNQ_ERR_NULL, "k, wk, k_fp8 and k_scale are required");
+  if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
+  const void* a16[] = {q, k, wq, wk, cos, sin};
+  for (const void* ptr : a16)
+    if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+  if (!aligned(q_fp8, 8) || !aligned(k_fp8, 8) || !aligned(q_scale, 4) || !aligned(k_scale, 4))
+    return fail(RNQ_ERR_UNSUPPORTED, "codes 8-byte, scales 4-byte aligned");
+  const bool q_first = q_heads > 0;
+  RowParams p = {};
+  p.x0 = (const uint16_t*)(q_first ? q : k);
+  p.w0 = (const uint16_t*)(q_first ? wq : wk);
+  p.c0 = q_first ? q_fp8 : k_fp8;
+  p.s0 = q_first ? q_scale : k_scale;
+  p.x1 = (const uint16_t*)(q_first ? k : nullptr);
+  p.w1 = (const uint16_t*)(q_first ? wk : nullptr);
+  p.c1 = q_first ? k_fp8 : nullptr;
+  p.s1 = q_first ? k_scale : nullptr;
+  p.cos = cos;
+  p.sin = sin;
+  p.total_rows = (uint32_t)(tokens * heads);
+  p.heads = (uint32_t)heads;
+  p.heads0 = (uint32_t)(q_first ? q_heads : kv_heads);
+  p.rope = (uint32_t)rope_dim;
+  p.eps = eps;
+  p.fp8_max = fp8_max;
+  return hip_status(launch_design(p, (uint32_t)rows_per_block, (int)head_dim, dtype == RNQ_BF16, (hipStream_t)stream),
+                    "rnq_baseline_qk_design");
 }
 
 }  // extern "C"

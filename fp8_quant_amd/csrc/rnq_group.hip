@@ -9,8 +9,10 @@
 // Mapping: one 256-thread workgroup per row; thread i owns 16-byte chunks
 // i, i+256, ... (KC of them). A group of group_size elements is GL =
 // group_size / 8 consecutive chunks, i.e. GL consecutive lanes of one wave, so
-// its absmax is a DPP reduction over those lanes. The rope tail's pairs live
-// in different threads: the normalised tail goes through LDS (one barrier).
+// its absmax is a DPP reduction over those lanes. One group per row (GL = 0)
+// takes the row's absmax instead: each wave's maximum, then the four through
+// LDS (one more barrier). The rope tail's pairs live in different threads:
+// the normalised tail goes through LDS (one barrier).
 // Every global access is a buffer access with a row-uniform descriptor (lanes
 // past the row's end use offsets outside its range).
 #include "rnq_device.h"
@@ -27,6 +29,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   constexpr uint32_t kOutOfRange = 0x80000000u;
   __shared__ double part[GWV];
   __shared__ float tail_s[kMaxRope];
+  __shared__ float wmax[GWV];
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = tid >> 6;
   const uint32_t row = blockIdx.x;
@@ -128,12 +131,30 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   const uint32_t n_groups = p.N / p.group_size;
   const rsrc_t rq = make_rsrc(p.codes + (size_t)row * p.N, p.N);
   const rsrc_t rs = make_rsrc(p.scales + (size_t)row * n_groups, 4u * n_groups);
-#pragma unroll
-  for (int k = 0; k < KC; ++k) {
+  float row_amax = 0.0f;
+  if constexpr (GL == 0) {
+    // one group per row: the row's absmax (lanes past the row's end hold zeros)
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
-    const float amax = group_max<GL>(m);
+    for (int k = 0; k < KC; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
+    m = group_max<64>(m);
+    if ((tid & 63) == 0) wmax[wave] = m;
+    __syncthreads();
+    row_amax = wmax[0];
+#pragma unroll
+    for (int v = 1; v < GWV; ++v) row_amax = fmaxf(row_amax, wmax[v]);
+  }
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    float amax = row_amax;
+    if constexpr (GL > 0) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
+      amax = group_max<GL>(m);
+    }
     // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
     float scale;
     if (p.scale_by_rcp)
@@ -152,9 +173,14 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     cw.x = fp8x4(q[0], q[1], q[2], q[3], __float_as_uint(q[0]));
     cw.y = fp8x4(q[4], q[5], q[6], q[7], __float_as_uint(q[4]));
     buf_store8_nt(rq, ok[k] ? 8u * ch[k] : kOutOfRange, cw);
-    // the group's first lane stores its scale
-    const bool first = ok[k] && ch[k] % GL == 0;
-    buf_store4(rs, first ? 4u * (ch[k] / GL) : kOutOfRange, scale);
+    // the group's first lane stores its scale (chunk 0 for a whole-row group)
+    uint32_t soff = kOutOfRange;
+    if constexpr (GL > 0) {
+      if (ok[k] && ch[k] % GL == 0) soff = 4u * (ch[k] / GL);
+    } else {
+      if (ch[k] == 0) soff = 0;
+    }
+    buf_store4(rs, soff, scale);
   }
 }
 
@@ -162,6 +188,10 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
 
 template <class DT, int KC>
 static hipError_t launch_kc(const GroupQuantParams& p, dim3 g, hipStream_t s) {
+  if (p.group_size == p.N && (p.N > 512 || (p.N & (p.N - 1)) != 0)) {  // one group per row (not one wave's lanes)
+    hipLaunchKernelGGL((group_quant_kernel<DT, KC, 0>), g, dim3(GT), 0, s, p);
+    return hipGetLastError();
+  }
   switch (p.group_size / 8) {
     case 1: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 1>), g, dim3(GT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 2>), g, dim3(GT), 0, s, p); break;

@@ -138,6 +138,14 @@ inline bool fp8_clamp_needed(float fp8_max) {
   return e4m3_magnitude_host((double)fp8_max * (1.0 + 0x1p-20)) != e4m3_magnitude_host((double)fp8_max);
 }
 
+// Measurement baselines (rnq_baselines.hip): steps 2 and 3 of the unfused
+// norm -> rope -> quant plan, and the chapter 28 designs (rows_per_block rows
+// per workgroup, lookups staged once per workgroup).
+hipError_t launch_unfused_rope_quant(const uint16_t* normed, const float* cos, const float* sin, uint16_t* rotated,
+                                     uint8_t* codes, float* scales, uint32_t M, uint32_t N, uint32_t R,
+                                     uint32_t rows_per_token, float fp8_max, bool bf16, hipStream_t s);
+hipError_t launch_design(const RowParams& p, uint32_t rows_per_block, int D, bool bf16, hipStream_t s);
+
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);
 hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream);

@@ -310,6 +310,22 @@ def rmsnorm_fwd_bytes(rows, width, in_bytes=2, write_rstd=False) -> dict:
     return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
 
 
+def norm_rope_quant_bytes(rows, width, rope_dim, rows_per_token=1, group_size=None, in_bytes=2,
+                          unfused=False) -> dict:
+    """RMSNorm + RoPE + FP8 on [rows, width] rows with one scale per group (default: per row).
+    Fused: x, the weight row and one cos/sin row per token read, codes and scales written.
+    Unfused (three kernels, the ledger page's plan): the normalised and rotated rows are
+    also written and read back once each."""
+    g = width if group_size is None else group_size
+    tables = rows // rows_per_token
+    reads = rows * width * in_bytes + width * in_bytes + 2 * tables * (rope_dim // 2) * 4
+    writes = rows * width + rows * (width // g) * 4
+    if unfused:
+        reads += 2 * rows * width * in_bytes
+        writes += 2 * rows * width * in_bytes
+    return {"rows": rows, "reads": reads, "writes": writes, "total": reads + writes}
+
+
 def rope_bwd_bytes(rows, width, rope_dim, rows_per_token=1, in_bytes=2) -> dict:
     """Bytes at the boundary of ``rnq_rmsnorm_rope_bwd`` (rstd recomputed): x and grad_y
     read, the weight row and one cos/sin row per token read once, grad_x and fp32 grad_w

@@ -2,6 +2,9 @@
 
 * ``stats``   - per-kernel call count and durations from a ``--kernel-trace``
   run (``*_kernel_trace.csv``), as a short Markdown table;
+* ``counters`` - every (kernel, grid) of a run with its calibrated HBM read
+  and write bytes per dispatch (two ``--pmc`` passes, as for ``traffic``), as
+  a Markdown table;
 * ``traffic`` - HBM bytes per launch of the row kernel from two ``--pmc``
   passes (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled
   by what the same counter reads for a plain copy of known size, written as
@@ -11,6 +14,8 @@
 Usage::
 
     python -m fp8_quant_amd.profiling stats TRACE_CSV OUT_MD --command "..."
+    python -m fp8_quant_amd.profiling counters FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV \
+        COPY_BYTES OUT_MD --command "..."
     python -m fp8_quant_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV \
         COPY_BYTES OUT_JSON --kernel rows_kernel --grid 1310720 --command "..."
 """
@@ -63,7 +68,41 @@ def counter_per_dispatch(counter_csv: str, counter: str, kernel_sub: str, grid: 
     return statistics.median(vals.values())
 
 
-def write_stats_md(trace_csv: str, out_md: str, command: str, top: int = 12) -> None:
+def headline_lines(trace_csv: str, kernel_sub: str, grid: str, timed: int, bench_us=None, block: int = 500) -> list:
+    """The headline kernel's timed launches (the last ``timed`` of its dispatches at ``grid``):
+    duration statistics, gaps, the span per launch, and the median per stretch of ``block``
+    launches over the whole run (the onset-of-load transient)."""
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in _rows(trace_csv)
+                if kernel_sub in r["Kernel_Name"] and (r.get("Grid_Size_X") or r.get("Grid_Size")) == grid)
+    if len(ev) < timed:
+        return []
+    t = ev[-timed:]
+    d = sorted(e - s for s, e in t)
+    q = lambda f: d[min(len(d) - 1, int(f * len(d)))] / 1e3
+    gaps = sorted(t[i + 1][0] - t[i][1] for i in range(len(t) - 1))
+    span = (t[-1][1] - t[0][0]) / timed / 1e3
+    out = [
+        "",
+        f"Headline kernel (grid {grid} threads): {len(ev)} launches ({len(ev) - timed} warm-up + {timed} timed), "
+        "back to back.",
+        f"Over the {timed} timed launches: mean {statistics.mean(d) / 1e3:.2f} us, median {statistics.median(d) / 1e3:.2f} us,",
+        f"p10 {q(0.1):.2f} us, p90 {q(0.9):.2f} us; median gap between kernels {statistics.median(gaps) / 1e3:.2f} us;",
+        f"first start to last end / {timed} = {span:.2f} us per launch"
+        + (f" (the bench's own figure in this run: {bench_us:.2f} us)." if bench_us else "."),
+        "",
+        f"Duration by stretch of the whole run (median of each block of {block} launches, start time of the block):",
+        "",
+        "| start | median us |",
+        "|---|---|",
+    ]
+    t0 = ev[0][0]
+    for i in range(0, len(ev) - block + 1, block):
+        blk = ev[i : i + block]
+        out.append(f"| {(blk[0][0] - t0) / 1e6:.1f} ms | {statistics.median(e - s for s, e in blk) / 1e3:.2f} |")
+    return out
+
+
+def write_stats_md(trace_csv: str, out_md: str, command: str, top: int = 16, headline=None) -> None:
     st = kernel_stats(trace_csv)
     lines = [
         "# rocprofv3 kernel trace summary",
@@ -79,6 +118,48 @@ def write_stats_md(trace_csv: str, out_md: str, command: str, top: int = 12) -> 
             name = name[:87] + "..."
         lines.append(f"| `{name}` | {s['grid']} | {s['calls']} | {s['avg_ns'] / 1e3:.2f} | "
                      f"{s['median_ns'] / 1e3:.2f} | {s['min_ns'] / 1e3:.2f} | {s['max_ns'] / 1e3:.2f} |")
+    if headline:
+        lines += headline_lines(trace_csv, *headline)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_kernel(counter_csv: str, counter: str) -> dict:
+    """(kernel, grid) -> median over dispatches of the counter summed per dispatch."""
+    per = {}
+    for r in _rows(counter_csv):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Grid_Size") or r.get("Grid_Size_X"), r.get("Workgroup_Size", ""))
+        d = per.setdefault(key, {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: statistics.median(v.values()) for k, v in per.items()}
+
+
+def write_counters_md(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out_md, command) -> None:
+    cf = counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copy", None)
+    cw = counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copy", None)
+    f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    fetch, write = _per_kernel(fetch_csv, "FETCH_SIZE"), _per_kernel(write_csv, "WRITE_SIZE")
+    lines = [
+        "# HBM bytes per dispatch by kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)",
+        "",
+        f"Command: `{command}` (one pass per counter), and `python3 bench.py --calibrate-copy` under the same",
+        f"counters for the calibration: a {copy_bytes}-byte copy reads {cf:.0f} KiB and writes {cw:.0f} KiB as",
+        f"counted, so FETCH is scaled by {f_scale:.4f} and WRITE by {w_scale:.4f}.",
+        "",
+        "| kernel | grid (threads) | workgroup | read MB | written MB | total MB |",
+        "|---|---|---|---|---|---|",
+    ]
+    for key in sorted(fetch, key=lambda k: -fetch[k]):
+        if "copyBuffer" in key[0] or key not in write:
+            continue
+        rd = fetch[key] * 1024.0 * f_scale / 1e6
+        wr = write[key] * 1024.0 * w_scale / 1e6
+        name = key[0].replace("|", "\\|")
+        if len(name) > 80:
+            name = name[:77] + "..."
+        lines.append(f"| `{name}` | {key[1]} | {key[2]} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -126,6 +207,15 @@ def main(argv=None) -> int:
     a.add_argument("trace_csv")
     a.add_argument("out_md")
     a.add_argument("--command", required=True)
+    a.add_argument("--headline", nargs=3, metavar=("KERNEL", "GRID", "TIMED"),
+                   help="add the timed-launch statistics of this kernel at this grid")
+    a.add_argument("--bench-us", type=float, default=None)
+    c = sub.add_parser("counters")
+    for n in ("fetch_csv", "write_csv", "copy_fetch_csv", "copy_write_csv"):
+        c.add_argument(n)
+    c.add_argument("copy_bytes", type=int)
+    c.add_argument("out_md")
+    c.add_argument("--command", required=True)
     b = sub.add_parser("traffic")
     for n in ("fetch_csv", "write_csv", "copy_fetch_csv", "copy_write_csv"):
         b.add_argument(n)
@@ -137,7 +227,11 @@ def main(argv=None) -> int:
     b.add_argument("--command", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
-        write_stats_md(args.trace_csv, args.out_md, args.command)
+        hl = None if not args.headline else (args.headline[0], args.headline[1], int(args.headline[2]), args.bench_us)
+        write_stats_md(args.trace_csv, args.out_md, args.command, headline=hl)
+    elif args.cmd == "counters":
+        write_counters_md(args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv, args.copy_bytes,
+                          args.out_md, args.command)
     else:
         rec = write_traffic_json(args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv,
                                  args.copy_bytes, args.out_json, args.kernel, args.grid, args.command,

@@ -170,8 +170,9 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
  * x [M,N] in dtype; w [N]; cos, sin [M/rows_per_token, R/2] fp32 (NULL allowed
  * when R == 0); outputs codes [M,N] bytes (8-byte aligned), scales
  * [M, N/group_size] fp32, y [M,N] in dtype (optional, NULL = not written).
- * Requirements: N a multiple of 8, at most 16384; group_size a power of two in
- * [8, 512] dividing N (SHAPE if it does not divide, UNSUPPORTED otherwise);
+ * Requirements: N a multiple of 8, at most 16384; group_size = N (one scale per
+ * row) or a power of two in [8, 512] dividing N (SHAPE if it does not divide,
+ * UNSUPPORTED otherwise);
  * R = rope_dim a multiple of 16, R <= N, R <= 1024; M % rows_per_token == 0;
  * 0 < fp8_max <= 448; M < 2^31. 16-bit tensors and the table 16-byte aligned.
  */

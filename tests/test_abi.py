@@ -21,9 +21,12 @@ def _lib():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "rnq.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rnq_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in ("rnq.h", "rnq_baselines.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(rnq_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -135,7 +138,8 @@ def test_grouped_argument_validation():
     assert call(N=8192, g=1024) == 3  # above 512
     assert call(N=4096, g=4) == 3  # below 8
     assert call(N=16392, g=8) == 3  # row too wide
-    assert call(N=4100, g=4100, R=0) == 3  # divides, not a power of two
+    assert call(N=4100, g=4100, R=0) == 3  # one group per row, but N is not a multiple of 8
+    assert call(N=4104, g=4104, R=0, M=0) == 0  # one group per row of any width (nothing to launch)
     assert call(R=2048) == 3  # rope tail above 1024
     assert call(R=24) == 3  # not a multiple of 16
     assert call(R=130) == 3
@@ -212,3 +216,28 @@ def test_strided_entry_validation():
     assert nr(M=62) == 2
     assert nr(N=1024) == 3
     assert nr(M=0) == 0
+
+
+def test_baseline_entry_validation():
+    lib = _lib()
+
+    def unf(M=64, N=4096, R=128, rpt=1, fmax=448.0):
+        return lib.rnq_baseline_norm_rope_quant_unfused(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, R, rpt,
+                                                        1e-6, fmax, 0, None)
+
+    assert unf(N=4100) == 3
+    assert unf(R=130) == 3
+    assert unf(M=63, rpt=2) == 2
+    assert unf(fmax=0.0) == 4
+    assert unf(M=0) == 0
+    assert lib.rnq_baseline_norm_rope_quant_unfused(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 4096, 128, 1,
+                                                    1e-6, 448.0, 0, None) == 1
+
+    def des(rpb=8, Hq=32, Hk=8, D=128):
+        return lib.rnq_baseline_qk_design(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, Hq, Hk, D, D,
+                                          rpb, 1e-6, 448.0, 0, None)
+
+    assert des(rpb=3) == 2  # does not divide 40 heads
+    assert des(rpb=0) == 2
+    assert des(rpb=40, D=512) == 3  # 2560 threads
+    assert des(D=96) == 3

@@ -23,6 +23,8 @@ where M = tokens x heads, weight ``[N]``, cos/sin ``[tokens, rope_dim/2]``):
   [4096, 64] table
 * ``norm_rope_pos`` - ``norm_rope_fp16``'s shapes with cos/sin gathered through
   the random positions from a [8192, 32] table instead of one table row per row
+* ``nrq_4k`` - the chapter 13 ledger page's norm+rope+quant plan size: 4096 x 4096
+  bf16, rope 128, one FP8 scale per row (fused, or as three kernels)
 """
 
 from __future__ import annotations
@@ -112,6 +114,10 @@ WORKLOADS: dict[str, Workload] = {
             rope_dim=128, outlier_p=0.01, positions="segments:8", cache_rows=4096, fused_qkv=True,
             description="QK-norm + RoPE + FP8 on q/k views of a fused QKV output, 4096 tokens x (32+8) heads "
                         "x 128, positions of 8 packed sequences into a 4096-row cos/sin table",
+        ),
+        Workload(
+            "nrq_4k", "grouped", seed=1010, rows=4096, width=4096, rope_dim=128, group_size=4096,
+            description="RMSNorm + RoPE + per-row FP8 on 4096 x 4096 bf16 rows, rope 128 (the ledger page's plan)",
         ),
         Workload(
             "norm_rope_pos", "norm_rope", seed=1009, rows=16384, width=128, rope_dim=64,
