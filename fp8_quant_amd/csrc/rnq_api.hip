@@ -312,6 +312,8 @@ rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const floa
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (!(fp8_max > 0.0f && fp8_max <= 448.0f)) return fail(RNQ_ERR_ARG, "fp8_max must lie in (0, 448] (got %g)", (double)fp8_max);
   if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
+  if ((M / rows_per_token) * (rope_dim / 2) * 4 >= ((int64_t)1 << 31))
+    return fail(RNQ_ERR_UNSUPPORTED, "the cos/sin table must stay below 2 GiB");
   if (M == 0 || N == 0) return ok();
   if (!x || !w || !codes || !scales) return fail(RNQ_ERR_NULL, "x, w, codes and scales are required");
   if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");

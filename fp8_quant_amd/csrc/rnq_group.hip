@@ -52,6 +52,22 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     xr[k] = buf_load16_nt(rx, off[k]);
     wr[k] = buf_load16(rw, off[k]);
   }
+  // the rope tail's cos/sin values go out with the row: a thread's chunks are
+  // 256 apart and the tail is at most 128 chunks, so a thread owns at most one
+  // tail chunk and needs one set of 8 pair columns (other lanes read nothing)
+  const uint32_t R = p.rope, half = R / 2;
+  const uint32_t t0 = nch - R / 8, hc = R / 16;  // first tail chunk, chunks per half
+  uint32_t toff = kOutOfRange;
+#pragma unroll
+  for (int k = 0; k < KC; ++k)
+    if (ok[k] && R > 0 && ch[k] >= t0) {
+      const uint32_t j = ch[k] - t0;
+      toff = 4u * ((row / p.rows_per_token) * half + 8u * (j < hc ? j : j - hc));
+    }
+  const uint32_t table_bytes = R > 0 ? ((p.M - 1) / p.rows_per_token + 1) * half * 4u : 0u;
+  const rsrc_t rcos = make_rsrc(p.cos, table_bytes), rsin = make_rsrc(p.sin, table_bytes);
+  const float4 tc0 = buf_load16f(rcos, toff), tc1 = buf_load16f(rcos, toff + 16u);
+  const float4 ts0 = buf_load16f(rsin, toff), ts1 = buf_load16f(rsin, toff + 16u);
 
   // ---- sum of squares: fp64 (exact for 16-bit inputs); waves added in ascending order
   double acc = 0.0;
@@ -82,10 +98,8 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     for (int i = 0; i < 8; ++i) y[k][i] = DT::round((xf[i] * rstd) * wf[i]);
   }
 
-  // ---- RoPE on the last R columns: pair p <-> p + R/2, through LDS
-  const uint32_t R = p.rope;
+  // ---- RoPE on the last R columns: pair p <-> p + R/2, the other half through LDS
   if (R > 0) {
-    const uint32_t half = R / 2, t0 = nch - R / 8, hc = R / 16;  // first tail chunk, chunks per half
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       if (ok[k] && ch[k] >= t0) {
@@ -94,19 +108,13 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
         *(float4*)(d + 4) = make_float4(y[k][4], y[k][5], y[k][6], y[k][7]);
       }
     __syncthreads();
-    const size_t trow = (size_t)(row / p.rows_per_token) * half;
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       if (ok[k] && ch[k] >= t0) {
         const uint32_t j = ch[k] - t0;
         const bool lo_half = j < hc;
-        const uint32_t pj = lo_half ? j : j - hc;  // pair chunk index in [0, R/16)
-        const float* c8 = p.cos + trow + 8 * pj;
-        const float* s8 = p.sin + trow + 8 * pj;
-        const float4 ca = *(const float4*)c8, cb = *(const float4*)(c8 + 4);
-        const float4 sa = *(const float4*)s8, sb = *(const float4*)(s8 + 4);
-        const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-        const float ss[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+        const float cc[8] = {tc0.x, tc0.y, tc0.z, tc0.w, tc1.x, tc1.y, tc1.z, tc1.w};
+        const float ss[8] = {ts0.x, ts0.y, ts0.z, ts0.w, ts1.x, ts1.y, ts1.z, ts1.w};
         const float* other = tail_s + 8 * (lo_half ? j + hc : j - hc);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
