@@ -258,34 +258,57 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   }
 }
 
-// grad_w[j] = sum over b of partial[b, j] in a fixed order. One wave per
-// float4 column group: lane l adds the partial rows l, l + 64, l + 128, ...
-// in ascending order (RU rows' loads in flight at a time; rows past the last
-// are outside the buffer descriptor and read as zero), then the 64 lane sums
-// are added by a fixed xor butterfly.
-constexpr int RDW = 4;  // waves (column groups) per workgroup
-constexpr int RU = 8;   // partial rows in flight per lane
+// grad_w[j] = sum over b of partial[b, j] in a fixed order. A workgroup of 8
+// waves owns a strip of 32 columns (8 float4 groups) and every partial row:
+// lane (r, c) of wave w (r = lane / 8, c = lane % 8) adds the rows
+// 64 u + 8 w + r (u = 0, 1, ...) of column group c in ascending u, with 8
+// rows' loads in flight; each load instruction reads 8 whole 128-byte row
+// segments. Rows past the last are outside the buffer descriptor (zero). The
+// 8 row lanes of a column are then added by an xor butterfly, the 8 waves by
+// a pairwise tree in LDS.
+constexpr int RDW = 8;   // waves per workgroup
+constexpr int RU = 8;    // loads in flight per lane
+constexpr int RCQ = 8;   // float4 column groups per strip
 __global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __restrict__ partial, float* __restrict__ gw,
                                                             uint32_t blocks, uint32_t N) {
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t c4 = blockIdx.x * RDW + (threadIdx.x >> 6);  // float4 column group (wave-uniform)
-  if (4 * c4 >= N) return;
+  __shared__ float4 red[RDW][RCQ];
+  const uint32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t c = lane % RCQ, r = lane / RCQ;
+  const uint32_t c4 = blockIdx.x * RCQ + c;  // float4 column group
+  const bool ok = 4 * c4 < N;
   const rsrc_t rp = make_rsrc(partial, 4u * blocks * N);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (uint32_t b0 = 0; b0 < blocks; b0 += 64 * RU) {
     float4 v[RU];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) v[u] = buf_load16f(rp, 4u * ((b0 + 64u * u + lane) * N + 4u * c4));
+    for (int u = 0; u < RU; ++u) {
+      const uint32_t row = b0 + 64u * u + RCQ * wave + r;
+      v[u] = buf_load16f(rp, ok ? 4u * (row * N + 4u * c4) : 0x80000000u);
+    }
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
     }
   }
-  acc.x = group_sum<64>(acc.x);
-  acc.y = group_sum<64>(acc.y);
-  acc.z = group_sum<64>(acc.z);
-  acc.w = group_sum<64>(acc.w);
-  if (lane == 0) *(float4*)(gw + 4 * (size_t)c4) = acc;
+#pragma unroll
+  for (int m = RCQ; m < 64; m *= 2) {
+    acc.x += __shfl_xor(acc.x, m, 64);
+    acc.y += __shfl_xor(acc.y, m, 64);
+    acc.z += __shfl_xor(acc.z, m, 64);
+    acc.w += __shfl_xor(acc.w, m, 64);
+  }
+  if (r == 0) red[wave][c] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int h = RDW / 2; h >= 1; h /= 2) {
+    if (wave < (uint32_t)h && r == 0) {
+      const float4 o = red[wave + h][c];
+      float4& t = red[wave][c];
+      t.x += o.x; t.y += o.y; t.z += o.z; t.w += o.w;
+    }
+    __syncthreads();
+  }
+  if (tid < (uint32_t)RCQ && ok) *(float4*)(gw + 4 * (size_t)c4) = red[0][c];
 }
 
 // ----------------------------------------------------------------- launchers
@@ -362,7 +385,7 @@ hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream
 
 hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream) {
   const uint32_t cols4 = N / 4;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((cols4 + RDW - 1) / RDW), dim3(64 * RDW), 0, stream, partial, gw, blocks, N);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((cols4 + RCQ - 1) / RCQ), dim3(64 * RDW), 0, stream, partial, gw, blocks, N);
   return hipGetLastError();
 }
 
