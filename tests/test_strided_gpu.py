@@ -207,3 +207,23 @@ def test_strided_invalid_arguments_raise():
     with pytest.raises(TypeError):  # positions must be int32
         rnq.rnq_qk_norm_rope_fp8_ex(gpu(q), None, gpu(wq), None, gpu(cos), gpu(sin), q8, None, qs, None,
                                     positions=gpu(torch.arange(T)))
+
+
+@pytest.mark.parametrize("Hq,Hk", [(8, 8), (3, 1)])  # aligned passes, per-lane rows
+def test_token_stride_beyond_32_bits(Hq, Hk):
+    """Two tokens 2^31 + 8 elements apart (an 8.6 GB buffer): the input offsets are 64-bit."""
+    T, D, R = 2, 128, 128
+    stride = (1 << 31) + 8
+    q, k, _, wq, wk = _fused(T, Hq, Hk, D, seed=504 + Hq)
+    cos, sin = (torch.from_numpy(a) for a in workloads.rope_table(np.arange(T), R, 10000.0))
+    print(f"[strided] token stride 2^31 + 8, Hq{Hq} Hk{Hk}", flush=True)
+    buf = torch.empty(T * stride, dtype=torch.bfloat16, device="cuda")
+    view = buf.as_strided((T, Hq + Hk, D), (stride, D, 1))
+    view.copy_(gpu(torch.cat([q, k], 1)))
+    qv = buf.as_strided((T, Hq, D), (stride, D, 1))
+    kv = buf.as_strided((T, Hk, D), (stride, D, 1), Hq * D)
+    got = _run_ex(qv, kv, gpu(wq), gpu(wk), gpu(cos), gpu(sin), None, with_y=True)
+    del buf, view, qv, kv
+    torch.cuda.empty_cache()
+    ref = _oracle(q, k, wq, wk, cos, sin, np.arange(T))
+    compare_qk("stride 2^31+8", {"q": q, "k": k}, got, ref)
