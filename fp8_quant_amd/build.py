@@ -76,7 +76,7 @@ def build_test_programs(verbose: bool = False) -> list:
     out_dir = os.path.join(ROOT, "tests", "bin")
     os.makedirs(out_dir, exist_ok=True)
     built = []
-    for name in ("row_scalar_check",):
+    for name in ("row_scalar_check", "host_logic_check"):
         exe = os.path.join(out_dir, name)
         cmd = [cc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], "-I", INCLUDE, "-I", CSRC,
                os.path.join(src_dir, name + ".hip"), "-o", exe]

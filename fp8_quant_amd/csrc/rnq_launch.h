@@ -120,6 +120,19 @@ struct GroupQuantParams {
 
 hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream);
 
+// row / d for every row < 2^31 as (row * magic) >> shift (64-bit product):
+// shift = 31 + lg with 2^lg >= d, magic = ceil(2^shift / d). With e = magic *
+// d - 2^shift in [0, d): row * magic / 2^shift = row / d + row * e / (d *
+// 2^shift), and the second term is below 2^31 / 2^shift = 2^-lg <= 1 / d,
+// too small to carry row / d (fractional part at most (d - 1) / d) past the
+// next integer, so the floor is exact.
+inline void div_magic_for(uint32_t d, uint32_t& magic, uint32_t& shift) {
+  uint32_t lg = 0;
+  while ((1u << lg) < d) ++lg;
+  shift = 31 + lg;
+  magic = (uint32_t)((((uint64_t)1 << shift) + d - 1) / d);
+}
+
 // Host side: e4m3fn code magnitude of a positive value below 480 (nearest even).
 inline int e4m3_magnitude_host(double v) {
   if (v < 0x1p-6) return (int)nearbyint(v * 512.0);

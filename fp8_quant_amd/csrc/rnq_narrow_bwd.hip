@@ -218,12 +218,8 @@ static hipError_t launch_width(const WideBwdParams& p, hipStream_t s) {
 hipError_t launch_narrow_bwd(WideBwdParams p, bool bf16, hipStream_t stream) {
   if (!narrow_bwd_width(p.N) || p.rope > p.N || p.rope % 16 != 0) return hipErrorInvalidValue;
   if (p.rows_per_token == 0) p.rows_per_token = 1;
-  // row / rows_per_token by multiply-shift: shift = 31 + ceil(log2 d), magic =
-  // ceil(2^shift / d), exact for every row < 2^31
-  uint32_t lg = 0;
-  while ((1u << lg) < p.rows_per_token) ++lg;
-  p.div_shift = 31 + lg;
-  p.div_magic = (uint32_t)((((uint64_t)1 << p.div_shift) + p.rows_per_token - 1) / p.rows_per_token);
+  // row / rows_per_token by multiply-shift (exact for every row < 2^31)
+  div_magic_for(p.rows_per_token, p.div_magic, p.div_shift);
   const hipError_t e = bf16 ? launch_width<BF16>(p, stream) : launch_width<F16>(p, stream);
   if (e != hipSuccess) return e;
   return launch_dw_reduce(p.partial, p.gw, p.blocks, p.N, stream);

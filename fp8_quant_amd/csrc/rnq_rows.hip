@@ -16,12 +16,8 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   if (p.total_rows == 0) return hipSuccess;
   const uint32_t G = 64u / (uint32_t)(head_dim / 16);
   p.passes = (uint32_t)((p.total_rows + G - 1) / G);
-  // t = row / heads by multiply-shift: shift = 31 + ceil(log2 heads), magic = ceil(2^shift / heads);
-  // exact for every row < 2^31.
-  uint32_t lg = 0;
-  while ((1u << lg) < p.heads) ++lg;
-  p.div_shift = 31 + lg;
-  p.div_magic = (uint32_t)((((uint64_t)1 << p.div_shift) + p.heads - 1) / p.heads);
+  // t = row / heads by multiply-shift (exact for every row < 2^31)
+  div_magic_for(p.heads, p.div_magic, p.div_shift);
   // passes stay inside one token and one tensor when both head counts are
   // multiples of G (then total_rows is a multiple of G too: whole passes only)
   const bool aligned = p.heads % G == 0 && p.heads0 % G == 0;
