@@ -174,7 +174,8 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
  * row) or a power of two in [8, 512] dividing N (SHAPE if it does not divide,
  * UNSUPPORTED otherwise);
  * R = rope_dim a multiple of 16, R <= N, R <= 1024; M % rows_per_token == 0;
- * 0 < fp8_max <= 448; M < 2^31. 16-bit tensors and the table 16-byte aligned.
+ * 0 < fp8_max <= 448; M < 2^31; each of cos and sin below 2 GiB (UNSUPPORTED).
+ * 16-bit tensors and the table 16-byte aligned.
  */
 rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const float* cos, const float* sin,
                                         void* y, uint8_t* codes, float* scales, int64_t M, int64_t N,
