@@ -1,0 +1,104 @@
+"""Seeded random-shape sweeps of the entry points against the CPU oracle (on
+top of the hand-picked shapes of the other GPU tests). Every case prints its
+parameters before it runs; the shapes are small enough for the oracle to
+check every element."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_quant_amd as rnq
+import oracle
+import workloads
+
+from _parity import compare_qk, gpu, run_qk_gpu, oracle_qk, unproven_rows
+
+pytestmark = pytest.mark.gpu
+
+DT = {torch.bfloat16: "bf16", torch.float16: "fp16"}
+SEEDS = list(range(12))
+
+
+def _rand_qk_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128, 256, 512]))
+    R = int(rng.choice([r for r in (0, 16, 32, 64, D, D) if r <= D]))
+    T = int(rng.integers(1, 90))
+    Hq = int(rng.integers(0, 12))
+    Hk = int(rng.integers(0 if Hq else 1, 6))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float16
+    std = float(rng.choice([0.01, 1.0, 30.0]))
+    fp8_max = float(rng.choice([448.0, 448.0, 240.0, 57.0]))
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = (torch.randn(T, Hq, D, generator=g) * std).to(dtype)
+    k = (torch.randn(T, Hk, D, generator=g) * std).to(dtype)
+    wq = (1 + 0.2 * torch.randn(D, generator=g)).to(dtype)
+    wk = (1 + 0.2 * torch.randn(D, generator=g)).to(dtype)
+    cos, sin = workloads.rope_table(rng.integers(0, 100000, T), R, float(rng.choice([1e4, 1e6])))
+    return {"q": q, "k": k, "wq": wq, "wk": wk, "cos": torch.from_numpy(cos), "sin": torch.from_numpy(sin)}, fp8_max
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_qk_random_shapes(seed):
+    d, fp8_max = _rand_qk_case(seed)
+    print(f"[sweep] qk seed {seed}: q{tuple(d['q'].shape)} k{tuple(d['k'].shape)} rope {2 * d['cos'].shape[-1]} "
+          f"{DT[d['q'].dtype]} fp8_max {fp8_max}", flush=True)
+    got = run_qk_gpu(d, fp8_max=fp8_max, with_y=bool(seed % 2))
+    ref = oracle_qk(d, fp8_max=fp8_max)
+    compare_qk(f"qk seed {seed}", d, got, ref, DT[d["q"].dtype])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_grouped_random_shapes(seed):
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.choice([8, 16, 32, 64, 128, 256, 512]))
+    N = G * int(rng.integers(1, max(2, 16384 // G // 4)))
+    N = min(N, 16384)
+    R = int(rng.choice([r for r in (0, 16, 64, 128, 256, 1024) if r <= N]))
+    rpt = int(rng.choice([1, 2, 4]))
+    M = rpt * int(rng.integers(1, 12))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float16
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = (torch.randn(M, N, generator=g) * float(rng.choice([0.05, 1.0, 8.0]))).to(dtype)
+    w = (1 + 0.2 * torch.randn(N, generator=g)).to(dtype)
+    cos, sin = workloads.rope_table(rng.integers(0, 5000, M // rpt), R, 10000.0)
+    print(f"[sweep] grouped seed {seed}: x({M}, {N}) group {G} rope {R} rows/token {rpt} {DT[dtype]}", flush=True)
+    codes, scales, y = rnq.rmsnorm_rope_fp8_grouped(gpu(x), gpu(w), gpu(torch.from_numpy(cos)),
+                                                    gpu(torch.from_numpy(sin)), group_size=G, rows_per_token=rpt,
+                                                    return_y=True)
+    torch.cuda.synchronize()
+    ry, rc, rs = oracle.rmsnorm_rope_fp8_grouped(workloads.bits(x), workloads.bits(w), cos, sin, G, 1e-6, 448.0,
+                                                 DT[dtype], rpt)
+    strict = ~unproven_rows(workloads.bits(x), DT[dtype])
+    gy, gc, gs = workloads.bits(y), codes.view(torch.uint8).cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(gy[strict], ry[strict])
+    assert np.array_equal(gc[strict], rc[strict])
+    assert np.array_equal(gs[strict].view(np.uint32), rs[strict].view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", SEEDS[:8])
+def test_rope_bwd_random_shapes(seed):
+    rng = np.random.default_rng(3000 + seed)
+    N = int(rng.choice([64, 128, 256, 512]))
+    R = int(rng.choice([r for r in (0, 16, 32, 64, 128, 256, 512) if r <= N]))
+    rpt = int(rng.choice([1, 3, 8]))
+    M = rpt * int(rng.integers(1, 400))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float16
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = (torch.randn(M, N, generator=g) * float(rng.choice([0.1, 1.0, 4.0]))).to(dtype)
+    w = (1 + 0.2 * torch.randn(N, generator=g)).to(dtype)
+    gy = torch.randn(M, N, generator=g).to(dtype)
+    cos, sin = workloads.rope_table(rng.integers(0, 5000, M // rpt), R, 10000.0)
+    print(f"[sweep] rope bwd seed {seed}: x({M}, {N}) rope {R} rows/token {rpt} {DT[dtype]}", flush=True)
+    gx, gw = rnq.rmsnorm_rope_bwd(gpu(x), gpu(w), gpu(gy), gpu(torch.from_numpy(cos)), gpu(torch.from_numpy(sin)),
+                                  rows_per_token=rpt)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw, _ = oracle.rmsnorm_rope_bwd(workloads.bits(x), workloads.bits(w), workloads.bits(gy), cos, sin,
+                                                1e-6, DT[dtype], rpt)
+    from oracle import codecs
+    dx = codecs.dtype_to_f32(workloads.bits(gx), DT[dtype]).astype(np.float64)
+    err = np.abs(dx - ref_dx) / (np.abs(ref_dx) + np.sqrt((ref_dx**2).mean(axis=1, keepdims=True)))
+    errw = np.abs(gw.cpu().numpy() - ref_dw) / (np.abs(ref_dw) + np.sqrt((ref_dw**2).mean()))
+    assert err.max() <= 2e-2 and errw.max() <= 2e-2, (err.max(), errw.max())
