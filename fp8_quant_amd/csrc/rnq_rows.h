@@ -19,8 +19,9 @@
 //    earlier ones retire). Every wave runs the same number of passes; the few
 //    slots past the end repeat the final pass, which writes the same bytes
 //    again.
-//  * Software pipeline: the input chunks of the next NS - 1 passes and the
-//    cos/sin values of the next pass are in flight while a pass is computed.
+//  * Software pipeline: the input chunks of the next NS - 1 passes (with their
+//    cos/sin chunks on aligned rope passes) and, on per-lane rows, the cos/sin
+//    values of the next pass are in flight while a pass is computed.
 //    No memory access in the steady state is conditional (clamped indices,
 //    every lane of a row storing the same scale), so the in-order memory
 //    counter can be waited on precisely.
@@ -79,10 +80,12 @@ struct Loc {
   bool second;    // row of tensor 1 (k)
 };
 
-// A pass's input chunks and its cos/sin values.
+// A pass's input chunks (and, on aligned rope passes, this lane's chunk of the
+// token's cos and sin rows, loaded with them).
 struct Data {
   Loc loc;
   uint4 xa, xb;
+  uint4 cw, sw;
 };
 struct Table {
   float4 c0, c1, s0, s1;  // this lane's values (per-lane rows)
@@ -198,22 +201,26 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, 2u * G * D);
       d.xa = buf_load16_nt(rx, 2u * pe_a);
       d.xb = buf_load16_nt(rx, 2u * pe_b);
+      if constexpr (STAGED) {
+        // the token's cos and sin rows (wave-uniform descriptors), one chunk of
+        // each per lane, in flight with the input: the wait for a pass's input
+        // covers them, and it never waits on the previous pass's stores
+        const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, 4u * half);
+        const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, 4u * half);
+        d.cw = buf_load16(rc, tq);
+        d.sw = buf_load16(rs, tq);
+      }
     } else {
       const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + d.loc.xoff;
       d.xa = load_stream16(src + off_a);
       d.xb = load_stream16(src + off_b);
     }
   };
-  // every lane loads (plain lanes read the row start and ignore it)
+  // per-lane rows: every lane loads its own table values (plain lanes read the
+  // row start and ignore it); aligned rope passes load theirs with the input
   auto load_table = [&](Table& t, const Loc& r) {
     if constexpr (ROPE) {
       if constexpr (ALIGNED) {
-        // the token's cos and sin rows (wave-uniform descriptors), one chunk
-        // of each per lane; the rows go through LDS to the lanes that use them
-        const rsrc_t rc = make_rsrc(p.cos + (size_t)r.trow * half, 4u * half);
-        const rsrc_t rs = make_rsrc(p.sin + (size_t)r.trow * half, 4u * half);
-        t.cw = buf_load16(rc, tq);
-        t.sw = buf_load16(rs, tq);
       } else {
         const float* cp = p.cos + (size_t)r.trow * half + cs_off;
         const float* sp = p.sin + (size_t)r.trow * half + cs_off;
@@ -259,8 +266,8 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       // accesses complete in order, so the reads below see these writes and the
       // previous pass's reads are done before they land
       if (lane < q4) {
-        *(uint4*)(t_wave + 4 * lane) = t.cw;
-        *(uint4*)(t_wave + half + 4 * lane) = t.sw;
+        *(uint4*)(t_wave + 4 * lane) = s.cw;
+        *(uint4*)(t_wave + half + 4 * lane) = s.sw;
       }
     }
 
@@ -341,9 +348,6 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
         sdst[r.ri] = scale;
       }
     }
-    // the next pass's table rows go out after this pass's stores: at the next
-    // pass, only that pass's input loads were issued after them
-    if constexpr (STAGED) load_table(t, next);
   };
 
   constexpr int NS = STAGED ? NS_STAGED : 2;  // (two: the register table ring alternates)
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   Table tb[2];
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) load_data(d[k], pass_of(k));
-  load_table(tb[0], d[0].loc);
+  if constexpr (!STAGED) load_table(tb[0], d[0].loc);
 
   // ---- weights of both tensors, fp32, in LDS (every thread loads a chunk, so
   // that no global access is conditional; the first D / 8 threads store them)
