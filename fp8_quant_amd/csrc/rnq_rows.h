@@ -131,8 +131,17 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
   r.trow = r.tok;
   if constexpr (POS) {
     // positions outside [0, max_pos) read the last table row (never out of range)
-    r.trow = min((uint32_t)p.positions[r.tok], p.max_pos - 1);
-    if constexpr (ALIGNED) r.trow = __builtin_amdgcn_readfirstlane(r.trow);
+    if constexpr (ALIGNED) {
+      // a wave-uniform index: read it through the constant address space (the
+      // kernel never writes positions), which gives a scalar load; a vector
+      // load would make the first use of its value wait for every earlier
+      // vector access, the previous pass's stores included
+      typedef const __attribute__((address_space(4))) int32_t const_i32;
+      const int32_t v = ((const_i32*)p.positions)[r.tok];
+      r.trow = __builtin_amdgcn_readfirstlane(min((uint32_t)v, p.max_pos - 1));
+    } else {
+      r.trow = min((uint32_t)p.positions[r.tok], p.max_pos - 1);
+    }
   }
   return r;
 }
@@ -194,6 +203,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   const uint32_t q4 = half / 4, tq = 16u * (q4 ? lane % q4 : 0u);
   float* t_wave = t_lds + (STAGED ? wave * D : 0);
 
+  auto load_staged_table = [&](Data& d) {
+    const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, 4u * half);
+    const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, 4u * half);
+    d.cw = buf_load16(rc, tq);
+    d.sw = buf_load16(rs, tq);
+  };
   auto load_data = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, D, ALIGNED, POS>(p, pass, slot);
     if constexpr (ALIGNED) {
@@ -201,15 +216,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, 2u * G * D);
       d.xa = buf_load16_nt(rx, 2u * pe_a);
       d.xb = buf_load16_nt(rx, 2u * pe_b);
-      if constexpr (STAGED) {
-        // the token's cos and sin rows (wave-uniform descriptors), one chunk of
-        // each per lane, in flight with the input: the wait for a pass's input
-        // covers them, and it never waits on the previous pass's stores
-        const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, 4u * half);
-        const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, 4u * half);
-        d.cw = buf_load16(rc, tq);
-        d.sw = buf_load16(rs, tq);
-      }
+      // the token's cos and sin rows (wave-uniform descriptors), one chunk of
+      // each per lane, in flight with the input: the wait for a pass's input
+      // covers them, and it never waits on the previous pass's stores. (With a
+      // positions index the row number is itself a load: the table chunks then
+      // go out from the middle of the previous pass, see compute.)
+      if constexpr (STAGED && !POS) load_staged_table(d);
     } else {
       const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + d.loc.xoff;
       d.xa = load_stream16(src + off_a);
@@ -234,7 +246,8 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 
   // t: this pass's table values; aligned rope passes stage them in LDS and
   // then load the next pass's table (at `next`) into t.
-  auto compute = [&](const Data& s, Table& t, const Loc& next, auto opts) {
+  // nd: the next pass's data (positions mode: its table chunks are loaded here)
+  auto compute = [&](const Data& s, Table& t, Data& nd, auto opts) {
     constexpr bool GEN = decltype(opts)::gen;
     constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
     const Loc& r = s.loc;
@@ -260,6 +273,11 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     float y[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) y[e] = DT::round((xv[e] * rstd) * wv[e]);
+
+    // positions mode: the next pass's table chunks, now that its row number
+    // (a scalar load issued with its input) has arrived; still before this
+    // pass's stores
+    if constexpr (STAGED && POS) load_staged_table(nd);
 
     if constexpr (STAGED) {
       // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
@@ -358,6 +376,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   Table tb[2];
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) load_data(d[k], pass_of(k));
+  if constexpr (STAGED && POS) load_staged_table(d[0]);
   if constexpr (!STAGED) load_table(tb[0], d[0].loc);
 
   // ---- weights of both tensors, fp32, in LDS (every thread loads a chunk, so
@@ -390,10 +409,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       for (int k = 0; k < NS; ++k) {
         load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
         if constexpr (STAGED) {
-          compute(d[k], tb[0], d[(k + 1) % NS].loc, opts);
+          compute(d[k], tb[0], d[(k + 1) % NS], opts);
         } else {
           load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
-          compute(d[k], tb[k % 2], d[k].loc, opts);
+          compute(d[k], tb[k % 2], d[k], opts);
         }
       }
     }
@@ -403,10 +422,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       if (base + k < n) {
         const int kn = k + 1 < NS - 1 ? k + 1 : k;  // (the last one reloads its own table)
         if constexpr (STAGED) {
-          compute(d[k], tb[0], d[kn].loc, opts);
+          compute(d[k], tb[0], d[kn], opts);
         } else {
           if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
-          compute(d[k], tb[k % 2], d[k].loc, opts);
+          compute(d[k], tb[k % 2], d[k], opts);
         }
       }
     }
