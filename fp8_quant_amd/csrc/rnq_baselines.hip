@@ -83,7 +83,7 @@ __global__ __launch_bounds__(BT) void quant_rows_kernel(QuantRowsParams p) {
   }
   m = group_max<64>(m);
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
+  lds_barrier();
   float amax = wmax[0];
 #pragma unroll
   for (int v = 1; v < BT / 64; ++v) amax = fmaxf(amax, wmax[v]);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(1024) void design_kernel(DesignParams p) {
   }
   for (uint32_t i = tid; i < 2u * half; i += blockDim.x)
     t_s[i] = i < half ? p.cos[(size_t)tok * half + i] : p.sin[(size_t)tok * half + (i - half)];
-  __syncthreads();
+  lds_barrier();
 
   const bool active = r_in < p.rows_per_block;
   const uint32_t row = first + (active ? r_in : 0);

@@ -133,6 +133,16 @@ __device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global
+// memory, which on this target waits for every outstanding global load and
+// store of the wave (prefetches of the next rows included); the barriers here
+// only ever protect LDS data, so they wait for the wave's LDS accesses alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------ DPP reductions
 // dpp_ctrl values (GFX9 DPP): quad_perm [1,0,3,2] = 0xB1 (xor 1),
 // quad_perm [2,3,0,1] = 0x4E (xor 2), row_half_mirror = 0x141 (lane i <- 7-i

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   }
   acc = group_sum<64>(acc);
   if ((tid & 63) == 0) part[wave] = acc;
-  __syncthreads();
+  lds_barrier();
   double tot = part[0];
 #pragma unroll
   for (int v = 1; v < GWV; ++v) tot += part[v];
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
         *(float4*)d = make_float4(y[k][0], y[k][1], y[k][2], y[k][3]);
         *(float4*)(d + 4) = make_float4(y[k][4], y[k][5], y[k][6], y[k][7]);
       }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       if (ok[k] && ch[k] >= t0) {
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
     m = group_max<64>(m);
     if ((tid & 63) == 0) wmax[wave] = m;
-    __syncthreads();
+    lds_barrier();
     row_amax = wmax[0];
 #pragma unroll
     for (int v = 1; v < GWV; ++v) row_amax = fmaxf(row_amax, wmax[v]);

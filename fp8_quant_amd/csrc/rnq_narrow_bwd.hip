@@ -174,11 +174,11 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
     mine[0] = make_float4(dw[0], dw[1], dw[2], dw[3]);
     mine[1] = make_float4(dw[4], dw[5], dw[6], dw[7]);
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int h = NBW / 2; h >= 1; h /= 2) {
     for (uint32_t i = tid; i < (uint32_t)(h * D); i += NB) red[i] += red[i + h * D];
-    __syncthreads();
+    lds_barrier();
   }
   if (tid < (uint32_t)D) p.partial[(size_t)blockIdx.x * D + tid] = red[tid];
 }

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
     acc = group_sum<64>(acc);
     if ((tid & 63) == 0) part[j][wave] = acc;
   }
-  __syncthreads();
+  lds_barrier();
 
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
 // last row re-reads that row and writes its identical grad_x again, so no
 // access in the loop is conditional and the in-order memory counter is waited
 // on precisely. grad_w partials accumulate in ascending row order.
-template <class DT, int KC, int BT, int RB>
+template <class DT, int KC, int BT, int RB, bool SAVED>
 __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   constexpr int BW = BT / 64;
   constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
     const uint4 wc = w_s[ok[k] ? tid + BT * k : 0u];
     unpack8<DT>(ok[k] ? wc : make_uint4(0, 0, 0, 0), wf);
   };
-  __syncthreads();
+  lds_barrier();
 
   auto load_batch = [&](uint32_t first, uint4 (&xs)[RB][KC], uint4 (&gs)[RB][KC]) {
 #pragma unroll
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
                    uint4 (&gn)[RB][KC]) {
     load_batch(first + RB, xn_, gn);
     float rstd[RB];
-    if (p.rstd != nullptr) {
+    if constexpr (SAVED) {
 #pragma unroll
       for (int j = 0; j < RB; ++j) rstd[j] = p.rstd[min(first + (uint32_t)j, r1 - 1)];
     } else {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
         acc = group_sum<64>(acc);
         if ((tid & 63) == 0) part_d[parity][j][wave] = acc;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
         double tot = part_d[parity][j][0];
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
       dot = group_sum<64>(dot);
       if ((tid & 63) == 0) part_f[parity][j][wave] = dot;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       float tot = part_f[parity][j][0];
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __rest
     acc.w += __shfl_xor(acc.w, m, 64);
   }
   if (r == 0) red[wave][c] = acc;
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int h = RDW / 2; h >= 1; h /= 2) {
     if (wave < (uint32_t)h && r == 0) {
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __rest
       float4& t = red[wave][c];
       t.x += o.x; t.y += o.y; t.z += o.z; t.w += o.w;
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (tid < (uint32_t)RCQ && ok) *(float4*)(gw + 4 * (size_t)c4) = red[0][c];
 }
@@ -335,18 +335,18 @@ static hipError_t fwd_kc(const WideFwdParams& p, int kc, hipStream_t s) {
 #ifndef RNQ_BWD_BATCH
 #define RNQ_BWD_BATCH 2
 #endif
-template <class DT>
+template <class DT, bool SAVED>
 static hipError_t bwd_kc(const WideBwdParams& p, int kc, dim3 g, hipStream_t s) {
   constexpr int B = RNQ_BWD_BATCH;
   const size_t lds = 2 * (size_t)p.N;  // the weight row
   if (p.N <= 2048) {
-    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B>), g, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B, SAVED>), g, dim3(256), lds, s, p);
     return hipGetLastError();
   }
   switch (kc) {
-    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512, B>), g, dim3(512), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512, (B > 2 ? B / 2 : 1)>), g, dim3(512), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512, (B > 4 ? B / 4 : 1)>), g, dim3(512), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512, B, SAVED>), g, dim3(512), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512, (B > 2 ? B / 2 : 1), SAVED>), g, dim3(512), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512, (B > 4 ? B / 4 : 1), SAVED>), g, dim3(512), lds, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -378,7 +378,9 @@ uint32_t bwd_blocks(int64_t M, int64_t N) {
 hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream) {
   dim3 grid(p.blocks);
   const int kc = chunks_per_lane(p.N, p.N > 2048 ? 512 : 256);
-  hipError_t e = bf16 ? bwd_kc<BF16>(p, kc, grid, stream) : bwd_kc<F16>(p, kc, grid, stream);
+  const bool saved = p.rstd != nullptr;
+  hipError_t e = bf16 ? (saved ? bwd_kc<BF16, true>(p, kc, grid, stream) : bwd_kc<BF16, false>(p, kc, grid, stream))
+                      : (saved ? bwd_kc<F16, true>(p, kc, grid, stream) : bwd_kc<F16, false>(p, kc, grid, stream));
   if (e != hipSuccess) return e;
   return launch_dw_reduce(p.partial, p.gw, p.blocks, p.N, stream);
 }
