@@ -11,7 +11,9 @@
 //    rope tail and chunk j of the upper half (the lane owns both members of
 //    its 8 RoPE pairs, so no exchange is needed); a plain unit holds two
 //    adjacent chunks. A wave covers G = 64/L rows per "pass"; each wave-wide
-//    load covers whole 128-byte spans of 8 rows (D = 128).
+//    load covers whole 128-byte spans of 8 rows (D = 128). The fp8 codes
+//    leave as whole 16-byte chunks: two neighbouring rope lanes swap halves
+//    (one DPP move per dword) so that each store writes whole lines.
 //  * W waves take the passes round-robin (wave w takes w, w + W, w + 2W, ...),
 //    so the waves in flight work on one narrow window of the tensors and DRAM
 //    pages are used whole. W is about what stays resident, or more for large
@@ -63,10 +65,13 @@ constexpr int NS_STAGED = RNQ_ROWS_STAGES;
 static_assert(NS_STAGED >= 2, "at least the pass in use and the next one");
 
 // Variants of the pass loop chosen once per wave: GEN = per-pass branches for
-// fp8_max below 1 or a clamp that can bind; FULL = the rope tail is the whole row.
-template <bool GEN, bool FULL>
+// fp8_max below 1 or a clamp that can bind; FULL = the rope tail is the whole
+// row; XCH = codes stored as whole 16-byte chunks after a swap inside each
+// pair of rope lanes (aligned passes whose plain part and rope tail are both
+// multiples of 32 columns).
+template <bool GEN, bool FULL, bool XCH = false>
 struct Opts {
-  static constexpr bool gen = GEN, full = FULL;
+  static constexpr bool gen = GEN, full = FULL, xch = XCH;
 };
 
 // Where one lane's row of a pass lives.
@@ -80,8 +85,8 @@ struct Loc {
   bool second;    // row of tensor 1 (k)
 };
 
-// A pass's input chunks (and, on aligned rope passes, this lane's chunk of the
-// token's cos and sin rows, loaded with them).
+// A pass's input chunks (and, on aligned rope passes, this lane's piece of the
+// token's cos and sin rows, loaded with them: the first 4, 8 or 16 bytes).
 struct Data {
   Loc loc;
   uint4 xa, xb;
@@ -199,15 +204,27 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   }
   // aligned passes: element offsets of this lane's chunks from the pass's first row
   const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
-  // aligned rope passes: lane l < half / 4 carries chunk l of the cos row and of the sin row
-  const uint32_t q4 = half / 4, tq = 16u * (q4 ? lane % q4 : 0u);
+  // aligned rope passes: lane l carries bytes [TB l, TB l + TB) of the token's
+  // cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB bytes
+  // cover it, each byte read once; lanes past the row read zero)
+  constexpr uint32_t TB = D / 32 < 4 ? 4u : (uint32_t)(D / 32);
+  const uint32_t toff = TB * lane;
+  const bool t_lane = toff < 4u * half;
   float* t_wave = t_lds + (STAGED ? wave * D : 0);
 
   auto load_staged_table = [&](Data& d) {
     const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, 4u * half);
     const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, 4u * half);
-    d.cw = buf_load16(rc, tq);
-    d.sw = buf_load16(rs, tq);
+    if constexpr (TB == 4) {
+      d.cw.x = buf_load4(rc, toff);
+      d.sw.x = buf_load4(rs, toff);
+    } else if constexpr (TB == 8) {
+      const uint2 c = buf_load8(rc, toff), s2 = buf_load8(rs, toff);
+      d.cw.x = c.x, d.cw.y = c.y, d.sw.x = s2.x, d.sw.y = s2.y;
+    } else {
+      d.cw = buf_load16(rc, toff);
+      d.sw = buf_load16(rs, toff);
+    }
   };
   auto load_data = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, D, ALIGNED, POS>(p, pass, slot);
@@ -250,6 +267,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   auto compute = [&](const Data& s, Table& t, Data& nd, auto opts) {
     constexpr bool GEN = decltype(opts)::gen;
     constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
+    constexpr bool XCH = decltype(opts)::xch;
     const Loc& r = s.loc;
     const float* w = w_lds + (r.second ? D : 0);
 
@@ -283,9 +301,17 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
       // accesses complete in order, so the reads below see these writes and the
       // previous pass's reads are done before they land
-      if (lane < q4) {
-        *(uint4*)(t_wave + 4 * lane) = s.cw;
-        *(uint4*)(t_wave + half + 4 * lane) = s.sw;
+      if (t_lane) {
+        if constexpr (TB == 4) {
+          t_wave[lane] = __uint_as_float(s.cw.x);
+          t_wave[half + lane] = __uint_as_float(s.sw.x);
+        } else if constexpr (TB == 8) {
+          *(uint2*)(t_wave + 2 * lane) = make_uint2(s.cw.x, s.cw.y);
+          *(uint2*)(t_wave + half + 2 * lane) = make_uint2(s.sw.x, s.sw.y);
+        } else {
+          *(uint4*)(t_wave + 4 * lane) = s.cw;
+          *(uint4*)(t_wave + half + 4 * lane) = s.sw;
+        }
       }
     }
 
@@ -356,8 +382,25 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       float* sdst = r.second ? p.s1 : p.s0;
       if constexpr (ALIGNED) {
         const rsrc_t rq = make_rsrc(cdst, (uint32_t)(G * D));
-        buf_store8_nt(rq, ea, ca);
-        buf_store8_nt(rq, eb, cb);
+        if constexpr (XCH) {
+          // whole 16-byte chunks (each store instruction writes whole lines):
+          // in a pair of rope lanes (tail chunks 2m and 2m + 1, lanes l and
+          // l ^ 1) the even lane keeps its lower-half codes and takes its
+          // partner's, the odd lane does the same with the upper half; plain
+          // lanes already hold 16 contiguous codes
+          const bool odd = (u & 1u) != 0;
+          const uint32_t gx = odd ? ca.x : cb.x, gy = odd ? ca.y : cb.y;
+          const uint32_t tx = (uint32_t)__builtin_amdgcn_mov_dpp((int)gx, 0xB1, 0xF, 0xF, true);
+          const uint32_t ty = (uint32_t)__builtin_amdgcn_mov_dpp((int)gy, 0xB1, 0xF, 0xF, true);
+          const bool rot = FULL || rope_lane;
+          const uint4 o = !rot ? make_uint4(ca.x, ca.y, cb.x, cb.y)
+                          : odd ? make_uint4(tx, ty, cb.x, cb.y)
+                                : make_uint4(ca.x, ca.y, tx, ty);
+          buf_store16_nt(rq, rot && odd ? eb - 8u : ea, o);
+        } else {
+          buf_store8_nt(rq, ea, ca);
+          buf_store8_nt(rq, eb, cb);
+        }
         const rsrc_t rsc = make_rsrc(sdst + r.ri0, 4u * G);
         buf_store4(rsc, 4u * slot, scale);  // every lane of the row stores the same value
       } else {
@@ -430,10 +473,14 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       }
     }
   };
+  // (XCH only where codes are stored from a wave-uniform base)
+  constexpr bool XQ = QUANT && ALIGNED;
   if (QUANT && (p.clamp || !p.scale_by_rcp))
     run(Opts<true, false>{});
   else if (ROPE && R == (uint32_t)D)
-    run(Opts<false, true>{});
+    run(Opts<false, true, XQ>{});
+  else if (XQ && (D - R) % 32u == 0 && R % 32u == 0)
+    run(Opts<false, false, XQ>{});
   else
     run(Opts<false, false>{});
 }

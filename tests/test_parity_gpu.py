@@ -170,6 +170,32 @@ def test_qk_shapes(T, Hq, Hk, D, R):
     _check_qk(f"qk T{T} Hq{Hq} Hk{Hk} D{D} R{R}", d)
 
 
+@pytest.mark.parametrize(
+    "T,Hq,Hk,D,R,with_y",
+    [
+        # head counts multiples of the rows per pass (64 / (D / 16)): every pass
+        # lies inside one token and one tensor. The tail widths cover the
+        # table loads at 4, 8 and 16 bytes per lane (D <= 128, 256, 512), rope
+        # tails that fill the row, tails whose code chunks are swapped between
+        # lane pairs (plain part and tail multiples of 32 columns), and tails
+        # that keep two 8-byte code stores per lane (R = 16, 48).
+        (9, 16, 16, 64, 64, False),
+        (9, 16, 0, 64, 32, True),
+        (11, 8, 8, 128, 64, False),
+        (11, 8, 8, 128, 48, True),
+        (11, 8, 16, 128, 16, False),
+        (13, 4, 4, 256, 256, True),
+        (13, 4, 8, 256, 96, False),
+        (7, 2, 2, 512, 512, False),
+        (7, 2, 4, 512, 160, True),
+        (7, 6, 2, 512, 64, False),
+    ],
+)
+def test_qk_aligned_passes(T, Hq, Hk, D, R, with_y):
+    d = _qk_case(T, Hq, Hk, D, R, seed=T * 977 + Hq * 31 + Hk * 7 + D + R, outliers=0.01)
+    _check_qk(f"qk aligned T{T} Hq{Hq} Hk{Hk} D{D} R{R}", d, with_y=with_y)
+
+
 def test_qk_fp16_inputs_and_smaller_fp8_max():
     d = _qk_case(64, 4, 2, 128, 64, seed=77, dtype=torch.float16, std=3.0)
     _check_qk("qk fp16", d, fp8_max=448.0)
