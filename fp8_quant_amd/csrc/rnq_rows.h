@@ -388,14 +388,17 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
           // l ^ 1) the even lane keeps its lower-half codes and takes its
           // partner's, the odd lane does the same with the upper half; plain
           // lanes already hold 16 contiguous codes
+          // (each partner value is read by a DPP move that folds into the
+          // select: four instructions per lane)
           const bool odd = (u & 1u) != 0;
-          const uint32_t gx = odd ? ca.x : cb.x, gy = odd ? ca.y : cb.y;
-          const uint32_t tx = (uint32_t)__builtin_amdgcn_mov_dpp((int)gx, 0xB1, 0xF, 0xF, true);
-          const uint32_t ty = (uint32_t)__builtin_amdgcn_mov_dpp((int)gy, 0xB1, 0xF, 0xF, true);
+          const uint32_t pax = (uint32_t)__builtin_amdgcn_mov_dpp((int)ca.x, 0xB1, 0xF, 0xF, true);
+          const uint32_t pay = (uint32_t)__builtin_amdgcn_mov_dpp((int)ca.y, 0xB1, 0xF, 0xF, true);
+          const uint32_t pbx = (uint32_t)__builtin_amdgcn_mov_dpp((int)cb.x, 0xB1, 0xF, 0xF, true);
+          const uint32_t pby = (uint32_t)__builtin_amdgcn_mov_dpp((int)cb.y, 0xB1, 0xF, 0xF, true);
           const bool rot = FULL || rope_lane;
-          const uint4 o = !rot ? make_uint4(ca.x, ca.y, cb.x, cb.y)
-                          : odd ? make_uint4(tx, ty, cb.x, cb.y)
-                                : make_uint4(ca.x, ca.y, tx, ty);
+          const bool lo = !rot || !odd;  // keeps its own first 8 codes
+          const bool hi = !rot || odd;   // keeps its own last 8 codes
+          const uint4 o = make_uint4(lo ? ca.x : pbx, lo ? ca.y : pby, hi ? cb.x : pax, hi ? cb.y : pay);
           buf_store16_nt(rq, rot && odd ? eb - 8u : ea, o);
         } else {
           buf_store8_nt(rq, ea, ca);
