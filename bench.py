@@ -8,9 +8,10 @@ rotated so the working set (> 512 MB) does not stay in the 256 MB Infinity
 Cache between steps. The K timed steps are launched back to back with
 pre-marshalled arguments between two events on the launch stream, so the
 time per step is the kernel's own time (the host stays ahead of the GPU).
-The default warm-up (2000 steps, ~30 ms) runs past the GPU's power-management
-transient at the onset of load, during which kernels run up to ~30 % slower;
-the timed steps measure the steady state.
+Every path warms up for its warm-up steps and at least 40 ms of back-to-back
+launches, past the GPU's power-management transient at the onset of load
+(~15 ms, during which kernels run up to ~30 % slower); the timed steps
+measure the steady state.
 
 Prints ONE JSON line: achieved GB/s (algorithmic bytes / step time), % of the
 8 TB/s HBM peak, rows/s, the roofline of the kernel, the other paths of the
@@ -36,6 +37,7 @@ KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.h", "fp8_quant_amd/csrc/rnq_rows_
                   "fp8_quant_amd/csrc/rnq_rows.hip", "fp8_quant_amd/csrc/rnq_rows_quant.hip",
                   "fp8_quant_amd/csrc/rnq_device.h", "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
+WARM_MS = 40.0  # the onset-of-load transient lasts ~15 ms
 ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
 COPY_BYTES = 256 * 2**20  # size of the plain copy used to calibrate the HBM byte counters
 
@@ -64,14 +66,22 @@ def measured_traffic():
 # ------------------------------------------------------------------ GPU timing
 
 
-def _timed(torch, launches, steps, warmup):
-    """Warm up, then time ``steps`` back-to-back launches (rotating over the
-    prepared launchers) between two events on the launch stream; ms per step.
-    Each launcher holds pre-marshalled arguments, so the host enqueues a call in
-    a few microseconds and the GPU runs the kernels back to back."""
+def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS):
+    """Warm up (``warmup`` launches, and at least ``warm_ms`` of back-to-back
+    work, so that every path is timed past the power-management transient at
+    the onset of load, whatever its launch length), then time ``steps``
+    back-to-back launches (rotating over the prepared launchers) between two
+    events on the launch stream; ms per step. Each launcher holds
+    pre-marshalled arguments, so the host enqueues a call in a few
+    microseconds and the GPU runs the kernels back to back."""
     n = len(launches)
-    for i in range(warmup):
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
         launches[i % n]()
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()  # (keeps the host clock on the GPU's pace)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
