@@ -94,7 +94,6 @@ struct Data {
 };
 struct Table {
   float4 c0, c1, s0, s1;  // this lane's values (per-lane rows)
-  uint4 cw, sw;           // one 16-byte chunk of the token's cos and sin rows (aligned passes)
 };
 
 __device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) {

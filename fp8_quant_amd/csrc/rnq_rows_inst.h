@@ -16,8 +16,9 @@ static hipError_t launch_shape(const RowParams& p, bool aligned, dim3 grid, hipS
 }
 
 // One 16-byte chunk of each half of a unit per lane: 8 lanes own a 128-wide
-// row, so each wave-wide access covers whole 128-byte (input) / 64-byte
-// (codes) spans of 8 rows.
+// row, so each wave-wide input access covers whole 128-byte spans of 8 rows,
+// and each code store whole 128-byte rows (64-byte halves where the rope tail
+// does not allow the lane-pair swap).
 template <class DT, int MODE>
 static hipError_t launch_dt(const RowParams& p, int D, bool aligned, dim3 grid, hipStream_t s) {
   switch (D) {
