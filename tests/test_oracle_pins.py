@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import _ties
 import oracle
 from oracle import codecs
 from oracle.exact import fraction_to_f32, sum_squares_exact_mask, sum_squares_f32
@@ -225,6 +226,49 @@ def test_clamp_applies_for_smaller_fp8_max():
     _, codes, _ = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 240.0)
     lim = int(codecs.e4m3_encode(np.float32(240.0)))
     assert (codes & 0x7F).max() == lim
+
+
+@pytest.mark.parametrize("fp8_max", [448.0, 240.0])
+def test_codes_are_the_e4m3_of_the_correctly_rounded_quotient(fp8_max):
+    """On rows built to put y / scale on e4m3 rounding midpoints (where one
+    rounding more or less flips the code), every code equals the e4m3 encoding
+    of the exact rational y / scale rounded once to fp32 and clamped."""
+    y = _ties.tie_rows(fp8_max)
+    codes, scale = oracle.quantize_rows(y, fp8_max)
+    yv = codecs.bf16_to_f32(y)
+    n_ties = 0
+    for i in range(y.shape[0]):
+        sc = Fraction(float(scale[i]))
+        assert scale[i].tobytes() == _exact_div_f32(float(np.abs(yv[i]).max()), fp8_max).tobytes()
+        for j in range(y.shape[1]):
+            r = Fraction(float(yv[i, j])) / sc
+            q = fraction_to_f32(abs(r)) * np.float32(-1.0 if r < 0 else 1.0)
+            q = np.float32(min(max(float(q), -fp8_max), fp8_max))
+            assert codes[i, j] == codecs.e4m3_encode(q), (i, j, float(yv[i, j]))
+            n_ties += float(q) != 0.0
+    assert n_ties > 200
+
+
+@pytest.mark.parametrize("fp8_max", [448.0, 240.0])
+def test_exact_rmsnorm_rows_carry_the_ties_to_the_quantiser(fp8_max):
+    """Rows whose mean square is a power of 4 normalise exactly (eps = 0, w = 1:
+    y = x * 2^-k), so the tie structure reaches the quantiser intact; the
+    codes then equal the exact-rational ones."""
+    x = _ties.normalised_tie_rows(fp8_max)
+    w = _bf16(np.ones(128))
+    y, codes, scale = oracle.norm_rope_quant_rows(x, w, np.zeros((len(x), 0), F32), np.zeros((len(x), 0), F32),
+                                                  0.0, fp8_max)
+    xv, yv = codecs.bf16_to_f32(x), codecs.bf16_to_f32(y)
+    ratio = yv[:, 0] / xv[:, 0]
+    assert np.all(yv == xv * ratio[:, None])  # one power of two per row
+    assert np.all(np.log2(ratio) == np.round(np.log2(ratio)))
+    for i in range(len(x)):
+        sc = Fraction(float(scale[i]))
+        for j in range(128):
+            r = Fraction(float(yv[i, j])) / sc
+            q = fraction_to_f32(abs(r)) * np.float32(-1.0 if r < 0 else 1.0)
+            q = np.float32(min(max(float(q), -fp8_max), fp8_max))
+            assert codes[i, j] == codecs.e4m3_encode(q), (i, j)
 
 
 def test_qk_shares_the_token_row_across_heads():

@@ -18,6 +18,7 @@ import oracle
 import workloads
 from oracle import codecs
 
+import _ties
 from _parity import (
     assert_rows_match,
     compare_qk,
@@ -194,6 +195,26 @@ def test_qk_shapes(T, Hq, Hk, D, R):
 def test_qk_aligned_passes(T, Hq, Hk, D, R, with_y):
     d = _qk_case(T, Hq, Hk, D, R, seed=T * 977 + Hq * 31 + Hk * 7 + D + R, outliers=0.01)
     _check_qk(f"qk aligned T{T} Hq{Hq} Hk{Hk} D{D} R{R}", d, with_y=with_y)
+
+
+def _tie_case(bits, T, Hq, Hk):
+    x = torch.from_numpy(bits[: T * (Hq + Hk)].view(np.int16)).view(torch.bfloat16).reshape(T, Hq + Hk, 128)
+    one = torch.ones(128, dtype=torch.bfloat16)
+    return {"q": x[:, :Hq].contiguous(), "k": x[:, Hq:].contiguous(), "wq": one, "wk": one,
+            "cos": torch.zeros(T, 0), "sin": torch.zeros(T, 0)}
+
+
+@pytest.mark.parametrize("fp8_max", [448.0, 240.0])
+def test_qk_quotients_on_e4m3_midpoints(fp8_max):
+    """Rows that normalise exactly (mean square a power of 4, eps = 0, w = 1) and
+    put y / scale exactly on e4m3 rounding midpoints, where a code flips with
+    one rounding more or less: the kernel's quotient must be the correctly
+    rounded one. Head-aligned passes (8 q + 8 k heads) and per-lane rows (1 head)."""
+    bits = _ties.normalised_tie_rows(fp8_max)
+    n = len(bits)
+    for name, T, Hq, Hk in (("aligned", n // 16, 8, 8), ("per-lane rows", n, 1, 0)):
+        d = _tie_case(bits, T, Hq, Hk)
+        _check_qk(f"qk ties {name} fp8_max {fp8_max}", d, eps=0.0, fp8_max=fp8_max)
 
 
 def test_qk_fp16_inputs_and_smaller_fp8_max():
