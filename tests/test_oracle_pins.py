@@ -271,6 +271,21 @@ def test_exact_rmsnorm_rows_carry_the_ties_to_the_quantiser(fp8_max):
             assert codes[i, j] == codecs.e4m3_encode(q), (i, j)
 
 
+def test_clamp_binds_when_fp8_max_is_an_e4m3_midpoint():
+    """fp8_max = 232 lies halfway between the e4m3 values 224 and 240. Where
+    RN(amax / 232) rounds down, amax / scale exceeds 232 and the clamp brings
+    it back to 232, which encodes (ties to even) as 224; without the clamp it
+    would encode as 240."""
+    x = _rows(400, 128, 54)
+    w = _bf16(1 + 0.1 * np.random.default_rng(55).standard_normal(128))
+    c, s = _table(400, 64, 56)
+    y, codes, scale = oracle.norm_rope_quant_rows(x, w, c, s, 1e-6, 232.0)
+    amax = np.abs(codecs.bf16_to_f32(y)).max(axis=1)
+    over = [Fraction(float(a)) / Fraction(float(sc)) > 232 for a, sc in zip(amax, scale)]
+    assert 50 < sum(over) < 350  # the clamp binds on a good share of the rows
+    assert np.all((codes & 0x7F).max(axis=1) == codecs.e4m3_encode(np.float32(224.0)))
+
+
 def test_qk_shares_the_token_row_across_heads():
     """Every head of a token is rotated by that token's table row."""
     T, Hq, Hk, D = 5, 3, 2, 64

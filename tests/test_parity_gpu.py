@@ -197,6 +197,16 @@ def test_qk_aligned_passes(T, Hq, Hk, D, R, with_y):
     _check_qk(f"qk aligned T{T} Hq{Hq} Hk{Hk} D{D} R{R}", d, with_y=with_y)
 
 
+@pytest.mark.parametrize("fp8_max", [58.0, 232.0, 0.5])
+def test_qk_aligned_passes_with_a_binding_clamp_or_small_fp8_max(fp8_max):
+    """Head-aligned passes through the per-pass-branch variant of the loop: fp8_max on
+    an e4m3 rounding midpoint (the clamp binds on about half of the rows) or below 1
+    (the scale by IEEE division)."""
+    for T, Hq, Hk, D, R in ((11, 8, 8, 128, 128), (9, 16, 16, 64, 32), (7, 2, 4, 512, 160)):
+        d = _qk_case(T, Hq, Hk, D, R, seed=T * 131 + D + int(fp8_max), outliers=0.02)
+        _check_qk(f"qk aligned T{T} H{Hq}+{Hk} D{D} R{R} fp8_max {fp8_max}", d, fp8_max=fp8_max)
+
+
 def _tie_case(bits, T, Hq, Hk):
     x = torch.from_numpy(bits[: T * (Hq + Hk)].view(np.int16)).view(torch.bfloat16).reshape(T, Hq + Hk, 128)
     one = torch.ones(128, dtype=torch.bfloat16)
