@@ -76,26 +76,27 @@ def _lowest_bit(q: Fraction) -> int:
 
 
 def normalised_tie_rows(fp8_max: float, width: int = 128, ties_per_row: int = 16):
-    """Rows whose RMSNorm (eps = 0, w = 1) is exact: column 0 amax, then up to
-    ``ties_per_row`` tie values, then filler values (each at most amax) that
-    bring the sum of squares to width * 4^k, so rstd = 2^-k exactly and the
-    normalised row is the row times 2^-k (the ties keep their ratios to amax).
-    With 16 ties the smallest such k leaves a remainder the filler columns can
-    always hold (at most 3 S <= 51 amax^2, plus a few columns for the low bits
-    of the greedy completion). Returns bf16 bits [rows, width]."""
+    """Rows whose RMSNorm (eps = 0, w = 1) is the identity: column 0 amax, then up
+    to ``ties_per_row`` tie values, then filler values (each at most amax) that
+    bring the sum of squares to exactly ``width``, so mean(x^2) = 1, rstd = 1 and
+    the normalised row is the row itself (also when rows are laid side by side
+    into a wider row). amax is scaled by a power of two into [1.13, 2.26): with
+    16 ties the sum is then at most 17 amax^2 < width, and the rest fits the
+    filler columns (including the few the greedy completion spends on low bits).
+    Returns bf16 bits [rows, width]."""
     odd = _ODD[fp8_max]
     rows = []
     for a_odd in range(odd, 256, 2 * odd):
-        amax = Fraction(a_odd, 128)
+        amax = Fraction(a_odd)
+        while amax >= Fraction(226, 100):
+            amax /= 2
+        while amax < Fraction(113, 100):
+            amax *= 2
         # largest first, so that each row's values span as few binades as possible
         ys = sorted(tie_values(fp8_max, amax), key=abs, reverse=True)
         for i in range(0, len(ys), ties_per_row):
             vals = [amax] + [Fraction(y) for y in ys[i:i + ties_per_row]]
-            s = sum(v * v for v in vals)
-            k = -40
-            while Fraction(width) * Fraction(4) ** k < s:
-                k += 1
-            d = Fraction(width) * Fraction(4) ** k - s
+            d = Fraction(width) - sum(v * v for v in vals)
             fill = []
             if d > 0:
                 # fillers are multiples of 2^floor(L/2), L the lowest bit of d: their
@@ -106,9 +107,22 @@ def normalised_tie_rows(fp8_max: float, width: int = 128, ties_per_row: int = 16
                     fill.append(f)
                     d -= f * f
             if d != 0:
-                continue  # (no exact completion within the row: skip it)
+                raise AssertionError(f"no exact completion for amax {amax}")
             row = np.zeros(width, np.float32)
             allv = vals + fill
             row[: len(allv)] = [float(v) for v in allv]
             rows.append(row)
     return codecs.bf16_round(np.stack(rows))
+
+
+def lowest_square_bit(bits: np.ndarray) -> np.ndarray:
+    """Per row of bf16 bits: the exponent of the lowest set bit over the squares
+    of its nonzero values (a float64 sum of the squares is exact in any order
+    while the total stays below 2^(that + 53))."""
+    vals = codecs.bf16_to_f32(bits)
+    out = []
+    for row in vals:
+        low = [2 * _lowest_bit(abs(Fraction(float(v)))) for v in row if v != 0]
+        out.append(min(low) if low else 0)
+    return np.array(out)
+

@@ -16,6 +16,7 @@ import fp8_quant_amd as rnq
 import oracle
 import workloads
 
+import _ties
 from _parity import code_distance, gpu, ulp_distance_16, unproven_rows
 
 pytestmark = pytest.mark.gpu
@@ -118,6 +119,25 @@ def test_grouped_4k_sampled_rows():
 def test_grouped_shapes(M, N, R, group):
     x, w, cos, sin = _case(M, N, R, M * 31 + N)
     _check(f"M{M} N{N} R{R} g{group}", x, w, cos, sin, group)
+
+
+@pytest.mark.parametrize("fp8_max", [448.0, 240.0])
+def test_grouped_quotients_on_e4m3_midpoints(fp8_max):
+    """Rows with mean square 1 (RMSNorm with eps = 0 and w = 1 is then the
+    identity) whose y / scale land exactly on e4m3 rounding midpoints: 32 of
+    them side by side as 4096-wide rows with groups of 128 (each group one tie
+    row), and one per row with a single scale (group_size = N = 128). The
+    quotient must be the correctly rounded one for the codes to match."""
+    bits = _ties.normalised_tie_rows(fp8_max)
+    bits = bits[_ties.lowest_square_bit(bits) > 12 - 53]  # exact float64 sums at the 4096-wide total 2^12
+    n = (len(bits) // 32) * 32
+    wide = np.ascontiguousarray(bits[:n].reshape(n // 32, 4096))
+    assert len(wide) >= 2 and not unproven_rows(wide, "bf16").any()
+    for name, xb in (("4096-wide, groups of 128", wide), ("128-wide, one group", bits)):
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+        w = torch.ones(x.shape[1], dtype=torch.bfloat16)
+        z = torch.zeros(x.shape[0], 0)
+        _check(f"ties {name} fp8_max {fp8_max}", x, w, z, z, 128, eps=0.0, fp8_max=fp8_max)
 
 
 def test_grouped_fp16_rows_per_token_and_no_y():
