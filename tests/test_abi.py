@@ -62,6 +62,32 @@ def _qk(lib, **kw):
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails before any launch
 
 
+def test_error_messages_are_per_thread():
+    """rnq_last_error is thread-local: two threads that fail at the same time on
+    different arguments each read their own message (the library keeps no
+    shared mutable state)."""
+    import threading
+
+    lib = _lib()
+    gate = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, kw):
+        st = _qk(lib, **kw)
+        gate.wait()  # both calls have failed before either reads its message
+        seen[name] = (st, lib.rnq_last_error().decode())
+
+    threads = [threading.Thread(target=worker, args=("null", {})),
+               threading.Thread(target=worker, args=("odd", dict(q=FAKE, R=63)))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert seen["null"][0] == 1 and seen["odd"][0] == 2
+    assert seen["null"][1] != seen["odd"][1]
+    assert "rope" in seen["odd"][1].lower() and "rope" not in seen["null"][1].lower()
+
+
 def test_qk_argument_validation():
     lib = _lib()
     assert _qk(lib) == 1  # NULL pointers
