@@ -1,7 +1,6 @@
 """The ledger reproduces the pages' byte/FLOP models exactly, and the library's own counts."""
 
 import json
-import math
 import os
 
 import pytest

@@ -26,7 +26,6 @@ from _parity import (
     oracle_qk,
     run_qk_gpu,
     unproven_rows,
-    ulp_distance_16,
 )
 
 pytestmark = pytest.mark.gpu
