@@ -51,8 +51,10 @@ def bf16_to_f32(b) -> np.ndarray:
 
 
 def f16_round(x) -> np.ndarray:
-    """float32 -> float16 bits (uint16), IEEE round to nearest even."""
-    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    """float32 -> float16 bits (uint16), IEEE round to nearest even (values past
+    the fp16 range become infinities, as IEEE rounding prescribes)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def f16_to_f32(b) -> np.ndarray:
