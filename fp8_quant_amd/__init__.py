@@ -8,8 +8,23 @@ computation runs in the HIP kernels; there is no CPU path. If the library has
 not been built, the first call raises.
 
 Convenience wrappers (``qk_norm_rope_fp8``, ``rmsnorm``, ``rmsnorm_bwd``,
-``rmsnorm_rope``, ``rmsnorm_rope_fp8_grouped``) allocate the outputs with torch
-and call the same entry points.
+``rmsnorm_rope``, ``rmsnorm_rope_bwd``, ``rmsnorm_rope_fp8_grouped``) allocate
+the outputs with torch and call the same entry points; ``prepare_*`` functions
+marshal once and return a launcher for tight loops or graph capture;
+``fp8_quant_amd.autograd`` wraps RMSNorm and RMSNorm + RoPE as autograd
+Functions. For example, the attention prologue of 4096 tokens with 32 query
+and 8 key/value heads of width 128 (bf16 on the GPU, cos/sin fp32 [4096, 64])::
+
+    import fp8_quant_amd as rnq
+    q8, k8, q_scale, k_scale = rnq.qk_norm_rope_fp8(q, k, wq, wk, cos, sin)
+    # q8: float8_e4m3fn [4096, 32, 128], q_scale: float32 [4096, 32]; same for k
+
+and with q and k as views into a fused QKV projection output, each token's
+cos/sin row looked up by position::
+
+    q = qkv[:, :32 * 128].view(T, 32, 128); k = qkv[:, 32 * 128:40 * 128].view(T, 8, 128)
+    q8, k8, q_scale, k_scale = rnq.qk_norm_rope_fp8(q, k, wq, wk, cos_table, sin_table,
+                                                    positions=pos_int32)
 """
 
 from __future__ import annotations
