@@ -385,7 +385,7 @@ def main() -> int:
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the rows are independent and the path would shard by token with no exchange", file=sys.stderr)
         return 2
 
