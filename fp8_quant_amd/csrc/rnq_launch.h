@@ -39,6 +39,7 @@ struct RowParams {
   float scale_floor;   // RN(1e-4 / fp8_max)
   uint32_t scale_by_rcp;
   uint32_t clamp;       // clamp quotients to +-fp8_max before encoding
+  uint32_t code16;      // both code outputs 16-byte aligned: whole 16-byte code stores allowed
   uint32_t passes;      // groups of 64 / (D / 16) consecutive rows
   uint32_t waves;       // waves that take passes (round-robin)
   uint32_t per_wave;    // passes per wave (the last ones repeat the final pass)

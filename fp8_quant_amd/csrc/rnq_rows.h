@@ -475,13 +475,16 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       }
     }
   };
-  // (XCH only where codes are stored from a wave-uniform base)
+  // (XCH only where codes are stored from a wave-uniform base, to 16-byte aligned outputs)
   constexpr bool XQ = QUANT && ALIGNED;
+  const bool xch = XQ && p.code16 != 0;
   if (QUANT && (p.clamp || !p.scale_by_rcp))
     run(Opts<true, false>{});
-  else if (ROPE && R == (uint32_t)D)
+  else if (ROPE && R == (uint32_t)D && xch)
     run(Opts<false, true, XQ>{});
-  else if (XQ && (D - R) % 32u == 0 && R % 32u == 0)
+  else if (ROPE && R == (uint32_t)D)
+    run(Opts<false, true>{});
+  else if (xch && (D - R) % 32u == 0 && R % 32u == 0)
     run(Opts<false, false, XQ>{});
   else
     run(Opts<false, false>{});

@@ -35,6 +35,8 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.scale_floor = 1e-4f / p.fp8_max;
   p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;
   p.clamp = quant && fp8_clamp_needed(p.fp8_max) ? 1u : 0u;
+  // (the entry points accept 8-byte aligned code outputs; 16-byte code stores need 16)
+  p.code16 = ((uintptr_t)p.c0 % 16 == 0 && (uintptr_t)p.c1 % 16 == 0) ? 1u : 0u;
   // contiguous inputs unless the caller gave token strides
   if (p.xs0 == 0) p.xs0 = (uint64_t)p.heads0 * (uint64_t)head_dim;
   if (p.xs1 == 0) p.xs1 = (uint64_t)(p.heads - p.heads0) * (uint64_t)head_dim;

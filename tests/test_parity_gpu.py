@@ -206,6 +206,28 @@ def test_qk_aligned_passes_with_a_binding_clamp_or_small_fp8_max(fp8_max):
         _check_qk(f"qk aligned T{T} H{Hq}+{Hk} D{D} R{R} fp8_max {fp8_max}", d, fp8_max=fp8_max)
 
 
+def test_qk_code_outputs_8_byte_aligned():
+    """Code outputs that are 8- but not 16-byte aligned (allowed by the entry point)
+    take the two 8-byte stores per lane instead of the whole 16-byte chunks."""
+    for T, Hq, Hk, D, R in ((11, 8, 8, 128, 128), (9, 16, 16, 64, 32), (13, 4, 8, 256, 96)):
+        d = _qk_case(T, Hq, Hk, D, R, seed=T * 17 + D + R, outliers=0.01)
+        print(f"[parity] qk codes at +8 bytes: T{T} H{Hq}+{Hk} D{D} R{R}", flush=True)
+        dev = torch.device("cuda:0")
+        qb = torch.empty(T * Hq * D + 16, dtype=torch.uint8, device=dev)
+        kb = torch.empty(T * Hk * D + 16, dtype=torch.uint8, device=dev)
+        q8, k8 = qb[8:8 + T * Hq * D].view(T, Hq, D), kb[8:8 + T * Hk * D].view(T, Hk, D)
+        assert q8.data_ptr() % 16 == 8 and k8.data_ptr() % 16 == 8
+        qs = torch.empty(T, Hq, device=dev)
+        ks = torch.empty(T, Hk, device=dev)
+        rnq.prepare_qk_norm_rope_fp8(gpu(d["q"]), gpu(d["k"]), gpu(d["wq"]), gpu(d["wk"]), gpu(d["cos"]),
+                                     gpu(d["sin"]), q8, k8, qs, ks)()
+        torch.cuda.synchronize()
+        ref = oracle_qk(d)
+        assert np.array_equal(q8.cpu().numpy(), ref["q_codes"]) and np.array_equal(k8.cpu().numpy(), ref["k_codes"])
+        assert np.array_equal(qs.cpu().numpy().view(np.uint32), ref["q_scale"].view(np.uint32))
+        assert np.array_equal(ks.cpu().numpy().view(np.uint32), ref["k_scale"].view(np.uint32))
+
+
 def _tie_case(bits, T, Hq, Hk):
     x = torch.from_numpy(bits[: T * (Hq + Hk)].view(np.int16)).view(torch.bfloat16).reshape(T, Hq + Hk, 128)
     one = torch.ones(128, dtype=torch.bfloat16)
