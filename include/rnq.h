@@ -25,8 +25,10 @@
  *  - Alignment: x/q/k/y/grad tensors, weights and cos/sin must be 16-byte
  *    aligned; FP8 outputs 8-byte aligned; fp32 vectors 4-byte aligned.
  *  - Arithmetic: fp32 with IEEE rounding at every step and no fused
- *    multiply-add; the sum of squares of a row is the exact sum rounded once to
- *    fp32; rsqrt is 1/sqrt with both steps correctly rounded; the normalised
+ *    multiply-add; the sum of squares of a row is accumulated in fp64, which is
+ *    exact whenever the row's total stays below 2^53 times the lowest set bit
+ *    of its smallest nonzero square (every row of the test workloads), and is
+ *    rounded once to fp32; rsqrt is 1/sqrt with both steps correctly rounded; the normalised
  *    row and the rotated row are each rounded to the input dtype (nearest
  *    even); codes are round-to-nearest-even e4m3fn of clamp(y/scale, +-fp8_max).
  *  - Errors: every argument is validated before anything is enqueued; on a
