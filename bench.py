@@ -314,6 +314,30 @@ def _summary(r):
 # ---------------------------------------------------------------- CPU oracle
 
 
+def bench_floor(torch, total_bytes, steps, warmup):
+    """The memory floor for the headline's bytes: rnq_baseline_stream reading
+    2/3 and writing 1/3 of ``total_bytes`` (rounded to whole 2 KB blocks; the
+    headline moves 44.0 MB in and 21.6 MB out), no arithmetic, rotated like the
+    headline; and the cost of an empty launch."""
+    from fp8_quant_amd import baselines
+
+    src_bytes = (2 * total_bytes // 3) // 2048 * 2048
+    n_sets = _n_sets(src_bytes * 3 // 2)
+    dev = torch.device("cuda:0")
+    sets = [(torch.empty(src_bytes, dtype=torch.uint8, device=dev).fill_(i + 1),
+             torch.empty(src_bytes // 2, dtype=torch.uint8, device=dev)) for i in range(n_sets)]
+    ms = _timed(torch, [baselines.prepare_stream(a, b) for a, b in sets], steps, warmup)
+    ms_empty = _timed(torch, [baselines.prepare_stream(None)], steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    moved = src_bytes * 3 // 2
+    return {"stream_us": round(ms * 1e3, 3), "stream_bytes": moved,
+            "stream_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "stream_pct_of_peak": round(100.0 * moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+            "empty_launch_us": round(ms_empty * 1e3, 3),
+            "kernel": "rnq_baseline_stream (one 2 KB block in, 1 KB out per wave, 16-byte nontemporal accesses)"}
+
+
 def cpu_baseline(workload_name: str, budget_s: float = 10.0) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
     256-token chunks in order, over the whole workload again and again until
@@ -441,6 +465,7 @@ def main() -> int:
         },
     }
     if not args.no_other_paths:
+        out["floor"] = bench_floor(torch, head["bytes"], args.steps, args.warmup)
         paths = []
         steps, warm = max(10, args.steps // 4), max(2, args.warmup // 4)
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_small", steps, warm)))

@@ -80,6 +80,7 @@ EXPORTED_SYMBOLS = (
     "rnq_rmsnorm_rope_ex",
     "rnq_baseline_norm_rope_quant_unfused",
     "rnq_baseline_qk_design",
+    "rnq_baseline_stream",
 )
 
 RNQ_BF16 = 0
@@ -140,6 +141,8 @@ def load_library():
     lib.rnq_baseline_norm_rope_quant_unfused.restype = i32
     lib.rnq_baseline_qk_design.argtypes = [vp] * 10 + [i64] * 6 + [f32, f32, i32, vp]
     lib.rnq_baseline_qk_design.restype = i32
+    lib.rnq_baseline_stream.argtypes = [vp, i64, vp, vp]
+    lib.rnq_baseline_stream.restype = i32
     _lib = lib
     return lib
 

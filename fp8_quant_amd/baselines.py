@@ -3,6 +3,8 @@ marshalling only, as for the hot-path entry points."""
 
 from __future__ import annotations
 
+import ctypes
+
 from . import _dtype_code, _expect, _launcher, _ptr, _stream, _torch, load_library
 
 __all__ = [
@@ -10,6 +12,7 @@ __all__ = [
     "prepare_qk_design",
     "norm_rope_quant_unfused",
     "qk_design",
+    "prepare_stream",
 ]
 
 
@@ -81,3 +84,20 @@ def qk_design(q, k, wq, wk, cos, sin, *, rows_per_block, eps=1e-6, fp8_max=448.0
     prepare_qk_design(q, k, wq, wk, cos, sin, q8, k8 if Hk else None, qs, ks if Hk else None,
                       rows_per_block=rows_per_block, eps=eps, fp8_max=fp8_max)()
     return q8.view(torch.float8_e4m3fn), k8.view(torch.float8_e4m3fn), qs, ks
+
+
+def prepare_stream(src, dst=None, *, stream=None):
+    """The memory floor: reads all of ``src`` (its size a multiple of 2048 bytes) and
+    writes half as many bytes to ``dst``; ``src=None`` gives a launch of one empty
+    workgroup (the cost of a launch). Returns a zero-argument launcher."""
+    lib = load_library()
+    if src is None:
+        s = stream if stream is not None else _torch().cuda.current_stream()
+        return _launcher(lib.rnq_baseline_stream, (None, 0, None, ctypes.c_void_p(s.cuda_stream)))
+    nbytes = src.numel() * src.element_size()
+    if dst is None or dst.numel() * dst.element_size() < nbytes // 2:
+        raise ValueError("dst must hold at least half of src's bytes")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    return _launcher(lib.rnq_baseline_stream, (_ptr(src), nbytes, _ptr(dst), _stream(src, stream)))
+

@@ -506,4 +506,19 @@ rnq_status rnq_baseline_qk_design(const void* q, const void* k, const void* wq, 
                     "rnq_baseline_qk_design");
 }
 
+rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, void* stream) {
+  if (src_bytes < 0 || src_bytes % 2048 != 0)
+    return fail(RNQ_ERR_SHAPE, "src_bytes must be a non-negative multiple of 2048 (got %lld)", (long long)src_bytes);
+  if (src_bytes / 2048 >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "src_bytes / 2048 must stay below 2^31");
+  if (src_bytes > 0 && (!src || !dst)) return fail(RNQ_ERR_NULL, "src and dst are required");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(RNQ_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+  if (src_bytes > 0) {
+    const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (uintptr_t)src_bytes;
+    const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (uintptr_t)(src_bytes / 2);
+    if (s0 < d1 && d0 < s1) return fail(RNQ_ERR_ARG, "src and dst overlap");
+  }
+  return hip_status(launch_stream(src, dst, (uint32_t)(src_bytes / 2048), (hipStream_t)stream),
+                    "rnq_baseline_stream");
+}
+
 }  // extern "C"

@@ -298,4 +298,33 @@ hipError_t launch_design(const RowParams& rp, uint32_t rows_per_block, int D, bo
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ HBM floor
+
+// The memory floor of a byte pattern like the prologue's, for measurement: wave
+// w reads the 2 KB block w of src (two 16-byte chunks per lane, 1 KB apart) and
+// writes the 1 KB block w of dst (their XOR), with nontemporal buffer accesses
+// and nothing else.
+__global__ __launch_bounds__(256) void stream_kernel(const uint8_t* src, uint8_t* dst, uint32_t blocks) {
+  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6), lane = threadIdx.x & 63u;
+  if (w >= blocks) return;  // (whole waves)
+  const rsrc_t rs = make_rsrc(src + (size_t)w * 2048u, 2048u);
+  const rsrc_t rd = make_rsrc(dst + (size_t)w * 1024u, 1024u);
+  const uint4 a = buf_load16_nt(rs, 16u * lane);
+  const uint4 b = buf_load16_nt(rs, 1024u + 16u * lane);
+  buf_store16_nt(rd, 16u * lane, make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w));
+}
+
+// One workgroup that does nothing: the cost of a launch.
+__global__ void empty_kernel() {}
+
+hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s) {
+  if (blocks == 0) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+  } else {
+    hipLaunchKernelGGL(stream_kernel, dim3((blocks + 3) / 4), dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst,
+                       blocks);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace rnq

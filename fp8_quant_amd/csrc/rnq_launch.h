@@ -159,6 +159,8 @@ hipError_t launch_unfused_rope_quant(const uint16_t* normed, const float* cos, c
                                      uint8_t* codes, float* scales, uint32_t M, uint32_t N, uint32_t R,
                                      uint32_t rows_per_token, float fp8_max, bool bf16, hipStream_t s);
 hipError_t launch_design(const RowParams& p, uint32_t rows_per_block, int D, bool bf16, hipStream_t s);
+// src_bytes / 2048 blocks of the memory-floor kernel (0: one empty workgroup)
+hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s);
 
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);

@@ -47,6 +47,17 @@ rnq_status rnq_baseline_qk_design(const void* q, const void* k, const void* wq, 
                                   int64_t rope_dim, int64_t rows_per_block, float eps, float fp8_max, int dtype,
                                   void* stream);
 
+/*
+ * The HBM floor the prologue is measured against: a kernel with the same kind
+ * of traffic and no arithmetic. Reads src_bytes (a multiple of 2048) and
+ * writes src_bytes / 2 to dst: the 1 KB block b of dst is the bytewise XOR of
+ * the two 1 KB halves of the 2 KB block b of src (one wave per block, 16-byte
+ * nontemporal accesses). src_bytes == 0 launches one empty workgroup (the cost
+ * of a launch). src and dst 16-byte aligned and not overlapping (ARG);
+ * src_bytes / 2048 < 2^31.
+ */
+rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

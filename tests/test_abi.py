@@ -244,6 +244,16 @@ def test_strided_entry_validation():
     assert nr(M=0) == 0
 
 
+def test_stream_floor_validation():
+    lib = _lib()
+    f = lib.rnq_baseline_stream
+    assert f(FAKE, 1000, FAKE, None) == 2  # not a multiple of 2048
+    assert f(FAKE, -2048, FAKE, None) == 2
+    assert f(None, 2048, FAKE, None) == 1
+    assert f(ctypes.c_void_p(0x10008), 2048, ctypes.c_void_p(0x20000), None) == 3  # src not 16-byte aligned
+    assert f(ctypes.c_void_p(0x10000), 4096, ctypes.c_void_p(0x10800), None) == 4  # dst inside src
+
+
 def test_baseline_entry_validation():
     lib = _lib()
 

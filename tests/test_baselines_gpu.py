@@ -112,3 +112,19 @@ def test_designs_other_widths(D, R, Hq, Hk, rpbs):
          "wk": (1 + 0.1 * torch.randn(D, generator=g)).to(torch.bfloat16),
          "cos": torch.from_numpy(cos), "sin": torch.from_numpy(sin)}
     _design_equals_rows_kernel(f"D{D}", d, rpbs)
+
+
+def test_stream_floor_kernel():
+    """The memory-floor kernel writes, for every 2 KB block of src, the XOR of its two halves."""
+    g = torch.Generator("cpu").manual_seed(5)
+    src = torch.randint(0, 256, (7 * 2048,), dtype=torch.uint8, generator=g)
+    dst = torch.full((7 * 1024 + 64,), 0xAB, dtype=torch.uint8)
+    sg, dg = gpu(src), gpu(dst)
+    baselines.prepare_stream(sg, dg)()
+    baselines.prepare_stream(None)()  # one empty workgroup
+    torch.cuda.synchronize()
+    blocks = src.numpy().reshape(7, 2, 1024)
+    want = np.bitwise_xor(blocks[:, 0], blocks[:, 1]).reshape(-1)
+    got = dg.cpu().numpy()
+    assert np.array_equal(got[: 7 * 1024], want) and np.all(got[7 * 1024:] == 0xAB)
+
