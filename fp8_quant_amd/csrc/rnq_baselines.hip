@@ -81,7 +81,7 @@ __global__ __launch_bounds__(BT) void quant_rows_kernel(QuantRowsParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
   }
-  m = group_max<64>(m);
+  m = group_max_nonneg<64>(m);
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
   lds_barrier();
   float amax = wmax[0];
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(1024) void design_kernel(DesignParams p) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
-  const float amax = group_max<L>(m);
+  const float amax = group_max_nonneg<L>(m);
   float scale;
   if (p.scale_by_rcp)
     scale = amax >= 1e-4f ? div_by(amax, p.fp8_max, p.rcp_fp8_max) : p.scale_floor;

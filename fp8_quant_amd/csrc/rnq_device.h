@@ -192,17 +192,26 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Max over aligned groups of L lanes of non-negative finite values
-// (IEEE-2019 maximum: no input canonicalisation needed).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Max over aligned groups of L lanes of non-negative values (absolute values;
+// +0 included, no NaN). For such floats the order of the bit patterns read as
+// unsigned integers is the order of the values, so the lanes combine with an
+// unsigned maximum, which takes the DPP operand directly (one instruction per
+// step instead of a move and a float maximum).
 template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (L >= 2) v = __builtin_elementwise_maximum(v, dpp_f32<0xB1>(v));
-  if constexpr (L >= 4) v = __builtin_elementwise_maximum(v, dpp_f32<0x4E>(v));
-  if constexpr (L >= 8) v = __builtin_elementwise_maximum(v, dpp_f32<0x141>(v));
-  if constexpr (L >= 16) v = __builtin_elementwise_maximum(v, dpp_f32<0x140>(v));
-  if constexpr (L >= 32) v = __builtin_elementwise_maximum(v, __shfl_xor(v, 16, 64));
-  if constexpr (L >= 64) v = __builtin_elementwise_maximum(v, __shfl_xor(v, 32, 64));
-  return v;
+__device__ __forceinline__ float group_max_nonneg(float f) {
+  uint32_t v = __float_as_uint(f);
+  if constexpr (L >= 2) v = max(v, dpp_u32<0xB1>(v));
+  if constexpr (L >= 4) v = max(v, dpp_u32<0x4E>(v));
+  if constexpr (L >= 8) v = max(v, dpp_u32<0x141>(v));
+  if constexpr (L >= 16) v = max(v, dpp_u32<0x140>(v));
+  if constexpr (L >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  if constexpr (L >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return __uint_as_float(v);
 }
 
 // ------------------------------------------------------------- row scalars

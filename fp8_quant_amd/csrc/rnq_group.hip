@@ -147,7 +147,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     for (int k = 0; k < KC; ++k)
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
-    m = group_max<64>(m);
+    m = group_max_nonneg<64>(m);
     if ((tid & 63) == 0) wmax[wave] = m;
     lds_barrier();
     row_amax = wmax[0];
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[k][i]));
-      amax = group_max<GL>(m);
+      amax = group_max_nonneg<GL>(m);
     }
     // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
     float scale;

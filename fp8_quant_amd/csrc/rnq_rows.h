@@ -357,7 +357,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[e]));
-      const float amax = group_max<L>(m);
+      const float amax = group_max_nonneg<L>(m);
       // scale = RN(max(amax, 1e-4) / fp8_max); amax is a 16-bit float value
       float scale;
       if (!GEN || p.scale_by_rcp)
