@@ -387,8 +387,8 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
           // l ^ 1) the even lane keeps its lower-half codes and takes its
           // partner's, the odd lane does the same with the upper half; plain
           // lanes already hold 16 contiguous codes
-          // (each partner value is read by a DPP move that folds into the
-          // select: four instructions per lane)
+          // (four DPP moves and four selects per lane; the selects taking the
+          // DPP operand directly, through inline assembly, measured no faster)
           const bool odd = (u & 1u) != 0;
           const uint32_t pax = (uint32_t)__builtin_amdgcn_mov_dpp((int)ca.x, 0xB1, 0xF, 0xF, true);
           const uint32_t pay = (uint32_t)__builtin_amdgcn_mov_dpp((int)ca.y, 0xB1, 0xF, 0xF, true);
