@@ -86,7 +86,8 @@ def sum_squares_f32(x32: np.ndarray) -> np.ndarray:
     """Per-row exact sum of squares, rounded once to float32. x32: [..., N] float32."""
     x32 = np.asarray(x32, dtype=np.float32)
     s64, exact = sum_squares_exact_mask(x32)
-    out = s64.astype(np.float32)  # single rounding where the float64 sum is exact
+    with np.errstate(over="ignore"):  # (sums past the fp32 range round to infinity, as IEEE prescribes)
+        out = s64.astype(np.float32)  # single rounding where the float64 sum is exact
     if not np.all(exact):
         flat_x = x32.reshape(-1, x32.shape[-1])
         flat_out = out.reshape(-1)
