@@ -24,6 +24,7 @@ _real = {
     "quantize_groups": prologue.quantize_groups,
     "truth_norm_rope": prologue.truth_norm_rope,
     "qk_norm_rope_fp8": prologue.qk_norm_rope_fp8,
+    "rmsnorm_rope": prologue.rmsnorm_rope,
     "rope_bwd_rotate": backward.rope_bwd_rotate,
     "_bwd_f64": backward._bwd_f64,
     "e4m3_encode": codecs.e4m3_encode,
@@ -121,6 +122,20 @@ def qk_table_row_per_row(q_bits, k_bits, wq_bits, wk_bits, cos, sin, eps=1e-6, f
     return out
 
 
+def rmsnorm_rope_table_row_per_row(x_bits, w_bits, cos, sin, eps=1e-6, dtype="bf16", rows_per_token=1, rows=None):
+    """Row r takes table row r (wrapped into the table) instead of r // rows_per_token."""
+    r = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows)
+    t = r % len(cos)
+    y, _, _ = prologue.norm_rope_quant_rows(x_bits, w_bits, np.asarray(cos)[t], np.asarray(sin)[t], eps, 448.0,
+                                            dtype, quant=False)
+    return y
+
+
+def rmsnorm_rope_subset_ignores_rows(x_bits, w_bits, cos, sin, eps=1e-6, dtype="bf16", rows_per_token=1, rows=None):
+    """The sampled rows' global indices are ignored (a sample takes table rows 0, 1, ...)."""
+    return _real["rmsnorm_rope"](x_bits, w_bits, cos, sin, eps, dtype, rows_per_token, None)
+
+
 def sum_squares_in_fp32_order(x32):
     x = np.asarray(x32, F32)
     acc = np.zeros(x.shape[:-1], F32)
@@ -187,6 +202,12 @@ CASES = [
      [lambda: pins.test_each_group_scale_is_its_own_absmax_over_fp8_max(64), pins.test_groups_are_independent]),
     ("table row per row, not per token", [(prologue, "qk_norm_rope_fp8", qk_table_row_per_row)],
      [pins.test_qk_shares_the_token_row_across_heads]),
+    ("path R: table row per row, not per token", [(prologue, "rmsnorm_rope", rmsnorm_rope_table_row_per_row)],
+     [lambda: pins.test_rmsnorm_rope_rows_of_a_token_share_its_table_row(4, 16, "bf16"),
+      pins.test_grouped_rows_of_a_token_share_its_table_row]),
+    ("path R: sampled rows read the sample's own table rows", [(prologue, "rmsnorm_rope",
+                                                                rmsnorm_rope_subset_ignores_rows)],
+     [lambda: pins.test_rmsnorm_rope_row_subset_equals_the_full_call(4)]),
     ("sum of squares accumulated in fp32", [(exact, "sum_squares_f32", sum_squares_in_fp32_order),
                                             (prologue, "sum_squares_f32", sum_squares_in_fp32_order),
                                             (pins, "sum_squares_f32", sum_squares_in_fp32_order)],

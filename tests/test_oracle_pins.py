@@ -303,6 +303,56 @@ def test_qk_shares_the_token_row_across_heads():
             assert out["k_scale"][t, h] == scale[0]
 
 
+def _shared_table_case(T, H, D, half, seed, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    if dtype == "fp16":
+        x = codecs.f16_round((2.0 * rng.standard_normal((T * H, D))).astype(F32))
+        w = codecs.f16_round((1 + 0.1 * rng.standard_normal(D)).astype(F32))
+    else:
+        x = _bf16(rng.standard_normal((T * H, D)))
+        w = _bf16(1 + 0.1 * rng.standard_normal(D))
+    c, s = _table(T, half, seed + 1)
+    return x, w, c, s
+
+
+@pytest.mark.parametrize("H,half,dtype", [(4, 16, "bf16"), (5, 32, "fp16"), (3, 8, "bf16")])
+def test_rmsnorm_rope_rows_of_a_token_share_its_table_row(H, half, dtype):
+    """Path R with rows_per_token = H: row r takes table row r // H, i.e. every
+    head of a token reads the token's one cos/sin row (chapter 28 page, module
+    docstring). Equal to the same call on a table with each row written out H
+    times, and to the QK entry's y (whose token sharing is pinned above)."""
+    T, D = 6, 64
+    x, w, c, s = _shared_table_case(T, H, D, half, 81, dtype)
+    shared = oracle.rmsnorm_rope(x, w, c, s, 1e-6, dtype, rows_per_token=H)
+    expanded = oracle.rmsnorm_rope(x, w, np.repeat(c, H, axis=0), np.repeat(s, H, axis=0), 1e-6, dtype)
+    assert np.array_equal(shared, expanded)
+    q = oracle.qk_norm_rope_fp8(x.reshape(T, H, D), None, w, None, c, s, dtype=dtype)
+    assert np.array_equal(shared, q["q_y"].reshape(T * H, D))
+    # a rotation by a different table row changes the result (the pin can see the map)
+    other = oracle.rmsnorm_rope(x, w, np.roll(c, 1, axis=0), np.roll(s, 1, axis=0), 1e-6, dtype, rows_per_token=H)
+    assert not np.array_equal(shared, other)
+
+
+@pytest.mark.parametrize("H", [1, 4])
+def test_rmsnorm_rope_row_subset_equals_the_full_call(H):
+    """``rows=`` (global row indices of a sample) gives exactly the sampled rows of the full call."""
+    T, D, half = 7, 64, 16
+    x, w, c, s = _shared_table_case(T, H, D, half, 83)
+    full = oracle.rmsnorm_rope(x, w, c, s, 1e-6, rows_per_token=H)
+    rows = np.array([T * H - 1, 0, 5, 2 * H + 1, 3]) % (T * H)
+    part = oracle.rmsnorm_rope(x[rows], w, c, s, 1e-6, rows_per_token=H, rows=rows)
+    assert np.array_equal(part, full[rows])
+
+
+def test_grouped_rows_of_a_token_share_its_table_row():
+    """The per-group quantiser inherits the same row -> table-row map."""
+    T, H, D, half = 4, 3, 128, 32
+    x, w, c, s = _shared_table_case(T, H, D, half, 85)
+    a = oracle.rmsnorm_rope_fp8_grouped(x, w, c, s, 32, rows_per_token=H)
+    b = oracle.rmsnorm_rope_fp8_grouped(x, w, np.repeat(c, H, axis=0), np.repeat(s, H, axis=0), 32)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
 # -------------------------------------------------------------------- backward pins
 
 
