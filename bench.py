@@ -38,6 +38,7 @@ KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.h", "fp8_quant_amd/csrc/rnq_rows_
                   "fp8_quant_amd/csrc/rnq_device.h", "fp8_quant_amd/csrc/rnq_launch.h", "fp8_quant_amd/build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
 WARM_MS = 40.0  # the onset-of-load transient lasts ~15 ms
+LEAD_MS = 0.5  # untimed work queued ahead of the start event
 ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
 COPY_BYTES = 256 * 2**20  # size of the plain copy used to calibrate the HBM byte counters
 
@@ -66,14 +67,21 @@ def measured_traffic():
 # ------------------------------------------------------------------ GPU timing
 
 
-def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS):
+def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS, lead_ms=LEAD_MS):
     """Warm up (``warmup`` launches, and at least ``warm_ms`` of back-to-back
     work, so that every path is timed past the power-management transient at
     the onset of load, whatever its launch length), then time ``steps``
     back-to-back launches (rotating over the prepared launchers) between two
     events on the launch stream; ms per step. Each launcher holds
     pre-marshalled arguments, so the host enqueues a call in a few
-    microseconds and the GPU runs the kernels back to back."""
+    microseconds and the GPU runs the kernels back to back.
+
+    After the warm-up's final synchronisation the queue is empty; a lead-in of
+    untimed launches (about ``lead_ms`` of GPU work, judged from the warm-up's
+    pace) is enqueued before the start event, so that the timed window opens
+    on a busy GPU with the host already ahead of it: the host-side latency of
+    submitting the first launch then falls outside the window, which matters
+    when only a few steps are timed."""
     n = len(launches)
     t0 = time.perf_counter()
     i = 0
@@ -83,11 +91,15 @@ def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS):
         if i % 256 == 0:
             torch.cuda.synchronize()  # (keeps the host clock on the GPU's pace)
     torch.cuda.synchronize()
+    per_launch_ms = (time.perf_counter() - t0) * 1e3 / max(i, 1)
+    lead = max(16, min(4096, math.ceil(lead_ms / max(per_launch_ms, 1e-4))))
+    for j in range(lead):
+        launches[(i + j) % n]()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        launches[i % n]()
+    for k in range(steps):
+        launches[(i + lead + k) % n]()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -97,9 +109,21 @@ def _n_sets(nbytes: int) -> int:
     return max(1, min(64, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
 
 
-def bench_qk(torch, rnq, workloads, ledger, name, steps, warmup):
+def input_hashes(workloads, d, names):
+    """SHA-256 of each named host input buffer (the bytes both the GPU and the oracle read)."""
+    out = {}
+    for k in names:
+        t = d.get(k)
+        if t is not None:
+            # 16-bit floats, fp32 and bytes through workloads.bits; integer indices as they are
+            out[k] = workloads.sha256(t.numpy() if not t.is_floating_point() else t)
+    return out
+
+
+def bench_qk(torch, rnq, workloads, ledger, name, steps, warmup, hashes=False):
     wl = workloads.WORKLOADS[name]
     d = workloads.generate(name)
+    sha = input_hashes(workloads, d, ("q", "k", "wq", "wk", "cos", "sin", "qkv", "positions")) if hashes else None
     T, Hq, Hk, D, R = d["tokens"], d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"]
     led = ledger.qk_bytes(T, Hq, Hk, D, R, write_y=wl.write_y)
     pos_cpu = d.get("positions")
@@ -138,6 +162,8 @@ def bench_qk(torch, rnq, workloads, ledger, name, steps, warmup):
                     for s in sets]
     ms = _timed(torch, launches, steps, warmup)
     out = {"workload": name, "ms": ms, "bytes": led["total"], "rows": led["rows"], "sets": n_sets}
+    if sha is not None:
+        out["inputs_sha256"] = sha
     del sets
     torch.cuda.empty_cache()
     return out
@@ -311,14 +337,25 @@ def _summary(r):
     return out
 
 
+def _with_floor(torch, summary, steps, warmup):
+    """A path's summary with the memory floor for its own byte count, measured in the same run."""
+    fl = bench_floor(torch, summary["bytes"], steps, warmup, with_empty=False)
+    summary["floor"] = {"stream_us": fl["stream_us"], "d2d_copy_us": fl["d2d_copy_us"],
+                        "stream_over_kernel": round(fl["stream_us"] / summary["us_per_call"], 3)}
+    return summary
+
+
 # ---------------------------------------------------------------- CPU oracle
 
 
-def bench_floor(torch, total_bytes, steps, warmup):
-    """The memory floor for the headline's bytes: rnq_baseline_stream reading
-    2/3 and writing 1/3 of ``total_bytes`` (rounded to whole 2 KB blocks; the
-    headline moves 44.0 MB in and 21.6 MB out), no arithmetic, rotated like the
-    headline; and the cost of an empty launch."""
+def bench_floor(torch, total_bytes, steps, warmup, with_empty=True):
+    """Memory floors for ``total_bytes`` of traffic, measured the same way as the
+    kernels: rnq_baseline_stream reading 2/3 and writing 1/3 of the bytes
+    (rounded to whole 2 KB blocks; the headline moves 44.0 MB in and 21.6 MB
+    out), no arithmetic, rotated like the headline; the runtime's own
+    device-to-device copy (torch ``copy_``, i.e. hipMemcpyAsync) of half the
+    bytes (read once, written once: the same total); and the cost of an empty
+    launch."""
     from fp8_quant_amd import baselines
 
     src_bytes = (2 * total_bytes // 3) // 2048 * 2048
@@ -327,51 +364,130 @@ def bench_floor(torch, total_bytes, steps, warmup):
     sets = [(torch.empty(src_bytes, dtype=torch.uint8, device=dev).fill_(i + 1),
              torch.empty(src_bytes // 2, dtype=torch.uint8, device=dev)) for i in range(n_sets)]
     ms = _timed(torch, [baselines.prepare_stream(a, b) for a, b in sets], steps, warmup)
-    ms_empty = _timed(torch, [baselines.prepare_stream(None)], steps, warmup)
     del sets
     torch.cuda.empty_cache()
     moved = src_bytes * 3 // 2
-    return {"stream_us": round(ms * 1e3, 3), "stream_bytes": moved,
-            "stream_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
-            "stream_pct_of_peak": round(100.0 * moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-            "empty_launch_us": round(ms_empty * 1e3, 3),
-            "kernel": "rnq_baseline_stream (one 2 KB block in, 1 KB out per wave, 16-byte nontemporal accesses)"}
+    copy_bytes = total_bytes // 2 // 256 * 256
+    n_sets = _n_sets(2 * copy_bytes)
+    csets = [(torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(i + 1),
+              torch.empty(copy_bytes, dtype=torch.uint8, device=dev)) for i in range(n_sets)]
+    ms_copy = _timed(torch, [(lambda a=a, b=b: b.copy_(a)) for a, b in csets], steps, warmup)
+    del csets
+    torch.cuda.empty_cache()
+    out = {"stream_us": round(ms * 1e3, 3), "stream_bytes": moved,
+           "stream_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
+           "stream_pct_of_peak": round(100.0 * moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "d2d_copy_us": round(ms_copy * 1e3, 3), "d2d_copy_bytes_moved": 2 * copy_bytes,
+           "d2d_copy_GB/s": round(2 * copy_bytes / (ms_copy * 1e-3) / 1e9, 1),
+           "d2d_copy_pct_of_peak": round(100.0 * 2 * copy_bytes / (ms_copy * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "kernel": "rnq_baseline_stream (one 2 KB block in, 1 KB out per wave, 16-byte nontemporal accesses); "
+                     "d2d copy: torch copy_ (hipMemcpyAsync device to device)"}
+    if with_empty:
+        out["empty_launch_us"] = round(_timed(torch, [baselines.prepare_stream(None)], steps, warmup) * 1e3, 3)
+    return out
 
 
-def cpu_baseline(workload_name: str, budget_s: float = 10.0) -> dict:
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    256-token chunks in order, over the whole workload again and again until
-    about ``budget_s`` seconds of CPU work have been timed (one pass at least
-    unless the budget ends first)."""
+_CPU = {}  # the sample a forked oracle worker reads (set before the pool forks)
+
+
+def _oracle_run(start_token: int, budget_s: float):
+    """Oracle calls on 256-token chunks from ``start_token`` on (wrapping), for about
+    ``budget_s`` seconds; returns (tokens done, seconds)."""
     import numpy as np
 
     import oracle
+
+    d = _CPU
+    T = d["T"]
+    tokens = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        lo = (start_token + tokens) % T
+        hi = min(lo + 256, T)
+        oracle.qk_norm_rope_fp8(d["q"][lo:hi], d["k"][lo:hi], d["wq"], d["wk"], d["cos"], d["sin"],
+                                tokens=np.arange(lo, hi))
+        tokens += hi - lo
+    return tokens, time.perf_counter() - t0
+
+
+def _oracle_worker(a):
+    return _oracle_run(*a)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(workload_name: str, single_s: float = 4.0, multi_s: float = 1.5, max_procs: int = 16) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample of the same workload,
+    256-token chunks at a time: once in this process (one thread: numpy's
+    elementwise loops are single-threaded), then in one forked process per
+    available core (at most ``max_procs``), each on its own token range, for
+    about ``multi_s`` seconds. Runs before anything touches the GPU (the
+    workers are plain forks that only run numpy). ``value`` is the all-cores
+    figure; the one-thread figure is kept beside it."""
+    import multiprocessing
+
     import workloads
     from fp8_quant_amd import ledger
 
     d = workloads.generate(workload_name)
     T = d["tokens"]
-    qb, kb = workloads.bits(d["q"]), workloads.bits(d["k"])
-    wq, wk = workloads.bits(d["wq"]), workloads.bits(d["wk"])
-    cos, sin = d["cos"].numpy(), d["sin"].numpy()
-    chunk = 256
-    tokens = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        lo = tokens % T
-        hi = min(lo + chunk, T)
-        oracle.qk_norm_rope_fp8(qb[lo:hi], kb[lo:hi], wq, wk, cos, sin, tokens=np.arange(lo, hi))
-        tokens += hi - lo
-    dt = time.perf_counter() - t0
-    b = ledger.qk_bytes(tokens, d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"])
+    _CPU.update(T=T, q=workloads.bits(d["q"]), k=workloads.bits(d["k"]), wq=workloads.bits(d["wq"]),
+                wk=workloads.bits(d["wk"]), cos=d["cos"].numpy(), sin=d["sin"].numpy())
+    Hq, Hk, D, R = d["q_heads"], d["kv_heads"], d["head_dim"], d["rope_dim"]
+    del d
+
+    def rate(tokens, dt):
+        b = ledger.qk_bytes(tokens, Hq, Hk, D, R)
+        return b["total"] / dt / 1e9, b["rows"] / dt, b["rows"]
+
+    tok1, dt1 = _oracle_run(0, single_s)
+    gbs1, rows1, nrows1 = rate(tok1, dt1)
+    single = {"value": round(gbs1, 6), "unit": "GB/s", "rows_per_s": round(rows1, 1), "cores": 1,
+              "sample": f"{tok1} tokens ({nrows1} rows) in {dt1:.1f} s"}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    procs = max(1, min(max_procs, avail))
+    multi = None
+    if procs > 1:
+        ctx = multiprocessing.get_context("fork")
+        t0 = time.perf_counter()
+        with ctx.Pool(procs) as pool:
+            res = pool.map_async(_oracle_worker, [((i * T) // procs, multi_s) for i in range(procs)]).get(
+                timeout=120)
+        wall = time.perf_counter() - t0
+        tokm = sum(t for t, _ in res)
+        span = max(dt for _, dt in res)
+        gbsm, rowsm, nrowsm = rate(tokm, span)
+        multi = {"value": round(gbsm, 6), "rows_per_s": round(rowsm, 1), "cores": procs, "tokens": tokm,
+                 "rows": nrowsm, "seconds": round(span, 2), "wall_with_fork_s": round(wall, 2)}
+    _CPU.clear()
+    best = multi if multi is not None else single
     return {
-        "value": round(b["total"] / dt / 1e9, 6),
+        "value": best["value"],
         "unit": "GB/s",
-        "rows_per_s": round(b["rows"] / dt, 1),
-        "cores": 1,
+        "rows_per_s": best["rows_per_s"],
+        "cores": best["cores"],
         "kind": "oracle",
-        "sample": f"{tokens} tokens ({tokens / T:.2f} passes over the {T} tokens of {workload_name}; "
-                  f"{b['rows']} rows) in 256-token chunks, numpy oracle (single thread), {dt:.1f} s",
+        "sample": (f"numpy oracle on 256-token chunks of {workload_name} ({T} tokens): "
+                   + (f"{multi['tokens']} tokens ({multi['rows']} rows) over {procs} processes, one per core, "
+                      f"each ~{multi_s:.1f} s on its own token range; " if multi else "")
+                   + f"one thread alone: {tok1} tokens ({nrows1} rows) in {dt1:.1f} s"),
+        "single_thread": single,
+        "cpu_model": cpu_model(),
+        "cores_available": avail,
     }
 
 
@@ -413,6 +529,9 @@ def main() -> int:
               "the rows are independent and the path would shard by token with no exchange", file=sys.stderr)
         return 2
 
+    # the CPU oracle first, before anything touches the GPU (its workers are forks)
+    cpu = None if args.no_cpu_baseline or args.fusion_only else cpu_baseline(args.workload)
+
     import torch
 
     import fp8_quant_amd as rnq
@@ -427,7 +546,7 @@ def main() -> int:
         fpaths, fsum = bench_fusion(torch, rnq, workloads, ledger, args.steps, args.warmup)
         print(json.dumps({"fusion": fsum, "paths": [_summary(r) for r in fpaths]}), flush=True)
         return 0
-    head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup)
+    head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup, hashes=True)
     wl = workloads.WORKLOADS[args.workload]
     ms = head["ms"]
     value = head["bytes"] / (ms * 1e-3) / 1e9
@@ -455,6 +574,7 @@ def main() -> int:
         "rows_per_s": round(head["rows"] / (ms * 1e-3), 1),
         "bytes_per_step": head["bytes"],
         "rotated_sets": head["sets"],
+        "inputs_sha256": head["inputs_sha256"],
         "roofline": {
             "bound": "hbm",
             "achieved": round(value, 2),
@@ -466,21 +586,30 @@ def main() -> int:
     }
     if not args.no_other_paths:
         out["floor"] = bench_floor(torch, head["bytes"], args.steps, args.warmup)
+        out["floor"]["kernel_over_stream_floor"] = round(ms * 1e3 / out["floor"]["stream_us"], 3)
+        out["floor"]["kernel_over_d2d_copy"] = round(ms * 1e3 / out["floor"]["d2d_copy_us"], 3)
         paths = []
         steps, warm = max(10, args.steps // 4), max(2, args.warmup // 4)
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_small", steps, warm)))
         paths += [_summary(r) for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, warm)]
-        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
+        paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16",
+                                                                 steps, warm)), steps, warm))
         paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
         paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_4k_fused", steps, warm)))
-        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos", steps, warm)))
+        paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos",
+                                                                 steps, warm)), steps, warm))
         fpaths, fsum = bench_fusion(torch, rnq, workloads, ledger, steps, warm)
         paths += [_summary(r) for r in fpaths]
         out["fusion"] = fsum
-        paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", max(5, steps // 5), 20)))
+        s64 = max(5, steps // 5)
+        big = _summary(bench_qk(torch, rnq, workloads, ledger, "qk_64k", s64, 20))
+        fl = bench_floor(torch, big["bytes"], s64, 20, with_empty=False)
+        big["floor"] = {"stream_us": fl["stream_us"], "d2d_copy_us": fl["d2d_copy_us"],
+                        "kernel_over_stream_floor": round(big["us_per_call"] / fl["stream_us"], 3)}
+        paths.append(big)
         out["other_paths"] = paths
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)
+    out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

@@ -249,11 +249,17 @@ def rnq_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale,
                              eps=eps, fp8_max=fp8_max, stream=stream)()
 
 
-def _launcher(fn, args):
+def _launcher(fn, args, *tensors):
+    """A zero-argument callable that enqueues ``fn(*args)``. The marshalled
+    arguments are raw device addresses, so the tensors they point into are kept
+    referenced by the launcher for as long as it exists."""
+    keep = tuple(t for t in tensors if t is not None)
+
     def launch():
         status = fn(*args)
         if status != 0:
             _check(status)
+    launch.tensors = keep
     return launch
 
 
@@ -288,7 +294,8 @@ def prepare_qk_norm_rope_fp8(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_sc
         _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale), _ptr(k_scale), _ptr(q_y), _ptr(k_y),
         T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
     )
-    return _launcher(lib.rnq_qk_norm_rope_fp8, args)
+    return _launcher(lib.rnq_qk_norm_rope_fp8, args, q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale,
+                     q_y, k_y)
 
 
 def rnq_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, q_y=None, k_y=None, *,
@@ -331,7 +338,8 @@ def prepare_qk_norm_rope_fp8_ex(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k
         _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale), _ptr(k_scale), _ptr(q_y), _ptr(k_y),
         T, Hq, Hk, D, 2 * half, eps, fp8_max, _dtype_code(q), _stream(q, stream),
     )
-    return _launcher(lib.rnq_qk_norm_rope_fp8_ex, args)
+    return _launcher(lib.rnq_qk_norm_rope_fp8_ex, args, q, k, wq, wk, cos, sin, positions, q_fp8, k_fp8,
+                     q_scale, k_scale, q_y, k_y)
 
 
 def rnq_rmsnorm_rope_ex(x, w, cos, sin, y, *, positions=None, rows_per_token: int = 1, eps: float = 1e-6,
@@ -365,7 +373,7 @@ def prepare_rmsnorm_rope_ex(x, w, cos, sin, y, *, positions=None, rows_per_token
     xp, xs = _token_view(xv, r, N, "x")
     args = (xp, xs, _ptr(w), _ptr(cos), _ptr(sin), _positions(positions, T), table_rows, _ptr(y), M, N, 2 * half,
             rows_per_token, eps, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_rope_ex, args)
+    return _launcher(lib.rnq_rmsnorm_rope_ex, args, x, w, cos, sin, positions, y)
 
 
 def rnq_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: float = 1e-6, stream=None) -> None:
@@ -384,7 +392,7 @@ def prepare_rmsnorm_rope(x, w, cos, sin, y, *, rows_per_token: int = 1, eps: flo
         _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
     args = (_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), M, N, 2 * half,
             rows_per_token, eps, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_rope, args)
+    return _launcher(lib.rnq_rmsnorm_rope, args, x, w, cos, sin, y)
 
 
 def rnq_rmsnorm_fwd(x, w, y, rstd=None, *, eps: float = 1e-6, stream=None) -> None:
@@ -399,7 +407,7 @@ def prepare_rmsnorm_fwd(x, w, y, rstd=None, *, eps: float = 1e-6, stream=None):
     _expect(y, x.dtype, (M, N), "y")
     _expect(rstd, torch.float32, (M,), "rstd")
     args = (_ptr(x), _ptr(w), _ptr(y), _ptr(rstd), M, N, eps, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_fwd, args)
+    return _launcher(lib.rnq_rmsnorm_fwd, args, x, w, y, rstd)
 
 
 def rnq_rmsnorm_bwd_workspace_size(M: int, N: int) -> int:
@@ -422,7 +430,7 @@ def prepare_rmsnorm_bwd(x, w, grad_y, grad_x, grad_w, workspace, rstd=None, *, e
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
             _ptr(workspace), ws_bytes, M, N, eps, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_bwd, args)
+    return _launcher(lib.rnq_rmsnorm_bwd, args, x, w, grad_y, rstd, grad_x, grad_w, workspace)
 
 
 def rnq_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, rstd=None, *, rows_per_token: int = 1,
@@ -449,7 +457,7 @@ def prepare_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(cos), _ptr(sin), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
             _ptr(workspace), ws_bytes, M, N, 2 * half, rows_per_token, eps, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_rope_bwd, args)
+    return _launcher(lib.rnq_rmsnorm_rope_bwd, args, x, w, grad_y, cos, sin, rstd, grad_x, grad_w, workspace)
 
 
 def rnq_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, group_size: int = 128,
@@ -477,7 +485,7 @@ def prepare_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, g
     _expect(scales, torch.float32, (M, N // group_size if group_size > 0 else 0), "scales")
     args = (_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(y), _ptr(codes), _ptr(scales), M, N, 2 * half,
             rows_per_token, group_size, eps, fp8_max, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_rmsnorm_rope_fp8_grouped, args)
+    return _launcher(lib.rnq_rmsnorm_rope_fp8_grouped, args, x, w, cos, sin, y, codes, scales)
 
 
 # ------------------------------------------------------- allocating wrappers

@@ -34,7 +34,7 @@ def prepare_norm_rope_quant_unfused(x, w, cos, sin, normed, rotated, codes, scal
     _expect(scales, torch.float32, (M,), "scales")
     args = (_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(normed), _ptr(rotated), _ptr(codes), _ptr(scales), M, N,
             2 * half, rows_per_token, eps, fp8_max, _dtype_code(x), _stream(x, stream))
-    return _launcher(lib.rnq_baseline_norm_rope_quant_unfused, args)
+    return _launcher(lib.rnq_baseline_norm_rope_quant_unfused, args, x, w, cos, sin, normed, rotated, codes, scales)
 
 
 def norm_rope_quant_unfused(x, w, cos, sin, *, rows_per_token=1, eps=1e-6, fp8_max=448.0):
@@ -68,7 +68,7 @@ def prepare_qk_design(q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale, *,
     _expect(k_scale, torch.float32, (T, Hk), "k_scale")
     args = (_ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(cos), _ptr(sin), _ptr(q_fp8), _ptr(k_fp8), _ptr(q_scale),
             _ptr(k_scale), T, Hq, Hk, D, 2 * half, rows_per_block, eps, fp8_max, _dtype_code(q), _stream(q, stream))
-    return _launcher(lib.rnq_baseline_qk_design, args)
+    return _launcher(lib.rnq_baseline_qk_design, args, q, k, wq, wk, cos, sin, q_fp8, k_fp8, q_scale, k_scale)
 
 
 def qk_design(q, k, wq, wk, cos, sin, *, rows_per_block, eps=1e-6, fp8_max=448.0):
@@ -99,5 +99,5 @@ def prepare_stream(src, dst=None, *, stream=None):
         raise ValueError("dst must hold at least half of src's bytes")
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("src and dst must be contiguous")
-    return _launcher(lib.rnq_baseline_stream, (_ptr(src), nbytes, _ptr(dst), _stream(src, stream)))
+    return _launcher(lib.rnq_baseline_stream, (_ptr(src), nbytes, _ptr(dst), _stream(src, stream)), src, dst)
 

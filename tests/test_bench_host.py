@@ -20,10 +20,52 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_cpu_baseline_fields():
-    cb = bench.cpu_baseline("qk_4k", budget_s=0.5)
-    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
+    cb = bench.cpu_baseline("qk_4k", single_s=0.3, multi_s=0.3, max_procs=2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s"
     assert cb["value"] > 0 and cb["rows_per_s"] > 0
     assert "tokens" in cb["sample"] and "numpy oracle" in cb["sample"]
+    assert cb["single_thread"]["cores"] == 1 and cb["single_thread"]["value"] > 0
+    assert cb["cores"] == min(2, cb["cores_available"]) and cb["cpu_model"]
+
+
+def test_cpu_baseline_single_process():
+    cb = bench.cpu_baseline("qk_4k", single_s=0.3, multi_s=0.3, max_procs=1)
+    assert cb["cores"] == 1 and cb["value"] == cb["single_thread"]["value"]
+
+
+def test_timer_queues_a_lead_in_before_the_start_event():
+    """The timed window opens on a busy queue: untimed launches go out after the
+    warm-up's last synchronisation and before the start event, and exactly
+    ``steps`` launches fall between the two events."""
+    log = []
+
+    class Ev:
+        def __init__(self, **kw):
+            pass
+
+        def record(self):
+            log.append("event")
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    class Cuda:
+        Event = Ev
+
+        @staticmethod
+        def synchronize():
+            log.append("sync")
+
+    class Torch:
+        cuda = Cuda
+
+    ms = bench._timed(Torch, [lambda: log.append("launch")], steps=7, warmup=3, warm_ms=0.0, lead_ms=0.0)
+    assert ms == 1.0 / 7
+    first_event = log.index("event")
+    last_sync_before = max(i for i, e in enumerate(log[:first_event]) if e == "sync")
+    assert log[last_sync_before + 1:first_event].count("launch") >= 16  # the lead-in
+    second_event = log.index("event", first_event + 1)
+    assert log[first_event + 1:second_event] == ["launch"] * 7
 
 
 def test_traffic_record_is_consistent():
