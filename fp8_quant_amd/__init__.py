@@ -45,6 +45,8 @@ __all__ = [
     "rnq_rmsnorm_bwd_workspace_size",
     "rnq_rmsnorm_rope_fp8_grouped",
     "rnq_rmsnorm_rope_bwd",
+    "rnq_rmsnorm_rope_bwd_noalloc",
+    "RNQ_NOALLOC_SCRATCH_BYTES",
     "rnq_qk_norm_rope_fp8_ex",
     "rnq_rmsnorm_rope_ex",
     "prepare_qk_norm_rope_fp8",
@@ -55,6 +57,7 @@ __all__ = [
     "prepare_rmsnorm_fwd",
     "prepare_rmsnorm_bwd",
     "prepare_rmsnorm_rope_bwd",
+    "prepare_rmsnorm_rope_bwd_noalloc",
     "qk_norm_rope_fp8",
     "rmsnorm",
     "rmsnorm_bwd",
@@ -81,10 +84,12 @@ EXPORTED_SYMBOLS = (
     "rnq_baseline_norm_rope_quant_unfused",
     "rnq_baseline_qk_design",
     "rnq_baseline_stream",
+    "rnq_rmsnorm_rope_bwd_noalloc",
 )
 
 RNQ_BF16 = 0
 RNQ_F16 = 1
+RNQ_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's static backward scratch (include/rnq.h)
 
 
 class RnqError(RuntimeError):
@@ -143,6 +148,8 @@ def load_library():
     lib.rnq_baseline_qk_design.restype = i32
     lib.rnq_baseline_stream.argtypes = [vp, i64, vp, vp]
     lib.rnq_baseline_stream.restype = i32
+    lib.rnq_rmsnorm_rope_bwd_noalloc.argtypes = [vp] * 8 + [i64] * 4 + [f32, i32, vp]
+    lib.rnq_rmsnorm_rope_bwd_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -458,6 +465,33 @@ def prepare_rmsnorm_rope_bwd(x, w, grad_y, cos, sin, grad_x, grad_w, workspace, 
     args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(cos), _ptr(sin), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
             _ptr(workspace), ws_bytes, M, N, 2 * half, rows_per_token, eps, _dtype_code(x), _stream(x, stream))
     return _launcher(lib.rnq_rmsnorm_rope_bwd, args, x, w, grad_y, cos, sin, rstd, grad_x, grad_w, workspace)
+
+
+def rnq_rmsnorm_rope_bwd_noalloc(x, w, grad_y, cos, sin, grad_x, grad_w, rstd=None, *, rows_per_token: int = 1,
+                                 eps: float = 1e-6, stream=None) -> None:
+    """rnq_rmsnorm_rope_bwd with the grad_w partials in the library's static device
+    scratch (no workspace, nothing allocated; calls that overlap on one GPU race)."""
+    prepare_rmsnorm_rope_bwd_noalloc(x, w, grad_y, cos, sin, grad_x, grad_w, rstd, rows_per_token=rows_per_token,
+                                     eps=eps, stream=stream)()
+
+
+def prepare_rmsnorm_rope_bwd_noalloc(x, w, grad_y, cos, sin, grad_x, grad_w, rstd=None, *, rows_per_token: int = 1,
+                                     eps: float = 1e-6, stream=None):
+    torch = _torch()
+    lib = load_library()
+    M, N = x.shape
+    half = 0 if cos is None else cos.shape[-1]
+    _expect(w, x.dtype, (N,), "w")
+    _expect(grad_y, x.dtype, (M, N), "grad_y")
+    _expect(grad_x, x.dtype, (M, N), "grad_x")
+    _expect(grad_w, torch.float32, (N,), "grad_w")
+    _expect(rstd, torch.float32, (M,), "rstd")
+    if cos is not None:
+        _expect(cos, torch.float32, (M // max(rows_per_token, 1), half), "cos")
+        _expect(sin, torch.float32, (M // max(rows_per_token, 1), half), "sin")
+    args = (_ptr(x), _ptr(w), _ptr(grad_y), _ptr(cos), _ptr(sin), _ptr(rstd), _ptr(grad_x), _ptr(grad_w),
+            M, N, 2 * half, rows_per_token, eps, _dtype_code(x), _stream(x, stream))
+    return _launcher(lib.rnq_rmsnorm_rope_bwd_noalloc, args, x, w, grad_y, cos, sin, rstd, grad_x, grad_w)
 
 
 def rnq_rmsnorm_rope_fp8_grouped(x, w, cos, sin, codes, scales, y=None, *, group_size: int = 128,

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "rnq.h"
@@ -350,12 +351,59 @@ size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
 
 namespace rnq {
 
-// Shared by the two backward entry points: validation, then the narrow-row
+// ------------------------------------------- allocation-free backward scratch
+// For callers that cannot allocate: the grad_w partials of
+// rnq_rmsnorm_rope_bwd_noalloc live in this file-scope device array (one copy
+// per GPU, held until the process ends). Host code never passes `scratch`
+// itself to a kernel (on the host it is only a stand-in for the symbol): each
+// device's address is looked up once with hipGetSymbolAddress and kept here.
+static __device__ __align__(256) float scratch[RNQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that runs `stream` (looked up on the
+// first call on that device, with that device current).
+static rnq_status scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RNQ_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(RNQ_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RNQ_OK;
+}
+
+// Shared by the three backward entry points: validation, then the narrow-row
 // kernel for widths 64..512 (with or without the RoPE tail) or the wide one.
+// With use_scratch the grad_w partials go to the static scratch above (looked
+// up after every argument has been validated) instead of the caller's workspace.
 static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void* w, const void* grad_y,
                                      const float* cos, const float* sin, const float* rstd, void* grad_x,
                                      float* grad_w, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
-                                     int64_t rope_dim, int64_t rows_per_token, float eps, int dtype, void* stream) {
+                                     int64_t rope_dim, int64_t rows_per_token, float eps, int dtype, void* stream,
+                                     bool use_scratch = false) {
   rnq_status s;
   if ((s = check_dtype(dtype)) != RNQ_OK) return s;
   if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
@@ -372,12 +420,28 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   if (!x || !w || !grad_y || !grad_x || !grad_w) return fail(RNQ_ERR_NULL, "x, w, grad_y, grad_x and grad_w are required");
   if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
   const size_t need = rnq_rmsnorm_bwd_workspace_size(M, N);
-  if (workspace == nullptr || workspace_bytes < need)
+  if (use_scratch) {
+    if (need > (size_t)RNQ_NOALLOC_SCRATCH_BYTES)
+      return fail(RNQ_ERR_WORKSPACE, "%s: M %lld, N %lld needs %zu bytes of scratch; the static scratch holds %zu", name,
+                  (long long)M, (long long)N, need, (size_t)RNQ_NOALLOC_SCRATCH_BYTES);
+  } else if (workspace == nullptr || workspace_bytes < need) {
     return fail(RNQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes, workspace);
-  const void* a16[] = {x, w, grad_y, grad_x, grad_w, workspace, cos, sin};
+  }
+  const void* a16[] = {x, w, grad_y, grad_x, grad_w, use_scratch ? nullptr : workspace, cos, sin};
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
   if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
+  const uint32_t blocks = bwd_blocks(M, N);
+  const uint32_t rows_per_block = (uint32_t)((M + blocks - 1) / blocks);
+  // the narrow kernel addresses a block's rows and the tables with 32-bit offsets
+  const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;
+  if (narrow_bwd_width(N) &&
+      ((int64_t)rows_per_block * N * 2 >= ((int64_t)1 << 31) || table_bytes >= ((int64_t)1 << 31)))
+    return fail(RNQ_ERR_UNSUPPORTED, "a block's rows or the cos/sin table exceed 2 GiB");
+  if (use_scratch) {
+    const rnq_status ss = scratch_for_stream((hipStream_t)stream, &workspace);
+    if (ss != RNQ_OK) return ss;
+  }
 
   WideBwdParams p = {};
   p.x = (const uint16_t*)x;
@@ -389,15 +453,11 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   p.partial = (float*)workspace;
   p.M = (uint32_t)M;
   p.N = (uint32_t)N;
-  p.blocks = bwd_blocks(M, N);
-  p.rows_per_block = (uint32_t)((M + p.blocks - 1) / p.blocks);
+  p.blocks = blocks;
+  p.rows_per_block = rows_per_block;
   p.eps = eps;
   if (!narrow_bwd_width(N)) return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
 
-  // the narrow kernel addresses a block's rows and the tables with 32-bit offsets
-  const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;
-  if ((int64_t)p.rows_per_block * N * 2 >= ((int64_t)1 << 31) || table_bytes >= ((int64_t)1 << 31))
-    return fail(RNQ_ERR_UNSUPPORTED, "a block's rows or the cos/sin table exceed 2 GiB");
   p.cos = cos;
   p.sin = sin;
   p.rope = (uint32_t)rope_dim;
@@ -423,6 +483,14 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
                                 int64_t rows_per_token, float eps, int dtype, void* stream) {
   return rmsnorm_bwd_common("rnq_rmsnorm_rope_bwd", x, w, grad_y, cos, sin, rstd, grad_x, grad_w, workspace,
                             workspace_bytes, M, N, rope_dim, rows_per_token, eps, dtype, stream);
+}
+
+rnq_status rnq_rmsnorm_rope_bwd_noalloc(const void* x, const void* w, const void* grad_y, const float* cos,
+                                        const float* sin, const float* rstd, void* grad_x, float* grad_w,
+                                        int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token, float eps,
+                                        int dtype, void* stream) {
+  return rmsnorm_bwd_common("rnq_rmsnorm_rope_bwd_noalloc", x, w, grad_y, cos, sin, rstd, grad_x, grad_w, nullptr,
+                            0, M, N, rope_dim, rows_per_token, eps, dtype, stream, true);
 }
 
 // ------------------------------------------------------ measurement baselines

@@ -37,7 +37,9 @@
  *    rnq_last_error() gives a per-thread message for the last failed call.
  *    A call with zero rows returns RNQ_OK and launches nothing.
  *  - Thread safety: no global mutable state apart from the per-thread error
- *    message; concurrent calls on different streams are independent.
+ *    message; concurrent calls on different streams are independent. (The
+ *    one exception is rnq_rmsnorm_rope_bwd_noalloc, which shares a static
+ *    device scratch array per GPU; see there.)
  */
 #ifndef RNQ_H_
 #define RNQ_H_
@@ -159,6 +161,35 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
                                 void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
                                 int64_t rope_dim, int64_t rows_per_token, float eps, int dtype,
                                 void* stream);
+
+/* Size of the library's static device scratch used by rnq_rmsnorm_rope_bwd_noalloc:
+ * 32 MiB, enough for the grad_w partials of every shape the backward accepts
+ * (at most 512 partial rows of N <= 16384 fp32 values). */
+#define RNQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * rnq_rmsnorm_rope_bwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels, results (bit for
+ * bit) and rules as rnq_rmsnorm_rope_bwd, minus workspace / workspace_bytes:
+ * the grad_w partials go to a file-scope device array of
+ * RNQ_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends). The call allocates nothing: on its first call on a device it
+ * looks up that device's copy of the array (hipGetSymbolAddress, the device
+ * of `stream`); later calls reuse the address.
+ * Errors: RNQ_ERR_WORKSPACE when rnq_rmsnorm_bwd_workspace_size(M, N) exceeds
+ * RNQ_NOALLOC_SCRATCH_BYTES (not reached for N <= 16384); RNQ_ERR_HIP when the
+ * lookup fails; otherwise as rnq_rmsnorm_rope_bwd.
+ * Concurrency: every call on one GPU uses that GPU's one array. Calls on one
+ * stream are ordered and safe; calls that overlap on one GPU (different
+ * streams, or threads without ordering) race on the array and give undefined
+ * grad_w. Nothing in the array needs to start at zero (every partial row a call
+ * reads is written by the same call first).
+ */
+rnq_status rnq_rmsnorm_rope_bwd_noalloc(const void* x, const void* w, const void* grad_y, const float* cos,
+                                        const float* sin, const float* rstd, void* grad_x, float* grad_w,
+                                        int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
+                                        float eps, int dtype, void* stream);
 
 /*
  * RMSNorm + partial NeoX RoPE + FP8 with one scale per group (chapter 13

@@ -201,6 +201,33 @@ def test_rope_bwd_argument_validation():
     assert call(dt=7) == 4
 
 
+def test_noalloc_bwd_argument_validation():
+    """The allocation-free backward validates every argument before it looks up its
+    static scratch (no HIP call is made for a rejected call)."""
+    lib = _lib()
+
+    def call(x=FAKE, cos=FAKE, M=4096, N=128, R=64, rpt=1, eps=1e-6, dt=0, rstd=None):
+        return lib.rnq_rmsnorm_rope_bwd_noalloc(x, FAKE, FAKE, cos, cos, rstd, FAKE, FAKE, M, N, R, rpt, eps, dt,
+                                                None)
+
+    assert call(x=None) == 1
+    assert call(cos=None) == 1
+    assert call(M=0, x=None) == 0
+    assert call(N=1024, R=64) == 3
+    assert call(N=16392, R=0) == 3  # wider than any row the backward takes
+    assert call(R=24) == 3
+    assert call(R=63) == 2
+    assert call(M=4095, rpt=2) == 2
+    assert call(M=-1) == 2
+    assert call(eps=-1.0) == 4
+    assert call(dt=7) == 4
+    assert call(rstd=ctypes.c_void_p(0x10002)) == 3  # rstd must be 4-byte aligned
+    # every shape the backward accepts fits the static scratch
+    assert lib.rnq_rmsnorm_bwd_workspace_size(8192, 16384) == rnq.RNQ_NOALLOC_SCRATCH_BYTES
+    assert lib.rnq_rmsnorm_bwd_workspace_size((1 << 31) - 1, 16384) <= rnq.RNQ_NOALLOC_SCRATCH_BYTES
+    assert "RNQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)" in open(os.path.join(ROOT, "include", "rnq.h")).read()
+
+
 def test_autograd_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     from fp8_quant_amd import autograd as rag
