@@ -24,10 +24,9 @@ import dataclasses
 import math
 
 __all__ = [
-    "ELEM_BYTES",
-    "Tensor",
-    "Kernel",
-    "Plan",
+    "BYTES_PER_ELEM",
+    "nbytes",
+    "plan_cost",
     "p4_plans",
     "QKShape",
     "p3_design",
@@ -41,133 +40,99 @@ __all__ = [
     "qk_flops",
 ]
 
-ELEM_BYTES = {"float32": 4, "float16": 2, "bfloat16": 2, "float8_e4m3fn": 1}
+BYTES_PER_ELEM = {"float32": 4, "float16": 2, "bfloat16": 2, "float8_e4m3fn": 1}
 
 
 # ----------------------------------------------------------- chapter 13 ledger model
+#
+# The page's counting rules: every kernel launch reads each of its inputs once
+# and writes each of its outputs once (so an intermediate costs a write in one
+# launch and a read in the next), and add / sub / mul / div / max and each
+# transcendental count one FLOP. Here a plan is a table with one row per launch
+# -- (bytes read, bytes written, FLOPs) -- written straight from those rules.
 
 
-@dataclasses.dataclass(frozen=True)
-class Tensor:
-    name: str
-    numel: int
-    dtype: str
-
-    def __post_init__(self):
-        if self.dtype not in ELEM_BYTES:
-            raise ValueError(f"unknown dtype {self.dtype!r}")
-        if self.numel < 0:
-            raise ValueError(f"{self.name}: negative element count")
-
-    @property
-    def nbytes(self) -> int:
-        return self.numel * ELEM_BYTES[self.dtype]
+def nbytes(count: int, dtype: str) -> int:
+    """Bytes of ``count`` elements of ``dtype``."""
+    if dtype not in BYTES_PER_ELEM:
+        raise ValueError(f"no element width for dtype {dtype!r}")
+    if count < 0:
+        raise ValueError(f"element count must be >= 0 (got {count})")
+    return count * BYTES_PER_ELEM[dtype]
 
 
-@dataclasses.dataclass(frozen=True)
-class Kernel:
-    name: str
-    reads: tuple
-    writes: tuple
-    flops: int
-
-    @property
-    def moved(self) -> int:
-        return sum(t.nbytes for t in self.reads) + sum(t.nbytes for t in self.writes)
-
-
-@dataclasses.dataclass(frozen=True)
-class Plan:
-    name: str
-    kernels: tuple
-
-    @property
-    def moved(self) -> int:
-        return sum(k.moved for k in self.kernels)
-
-    @property
-    def flops(self) -> int:
-        return sum(k.flops for k in self.kernels)
-
-    @property
-    def ai(self) -> float:
-        return self.flops / self.moved if self.moved else math.inf
+def plan_cost(label: str, launches) -> dict:
+    """Totals of a plan given as rows (bytes read, bytes written, FLOPs), one per launch."""
+    moved = sum(r + w for r, w, _ in launches)
+    flops = sum(f for _, _, f in launches)
+    return {"label": label, "kernels": len(launches), "moved": moved, "flops": flops,
+            "ai": flops / moved if moved else math.inf}
 
 
 def _scale_add(n: int, dt: str):
-    x, b, t, y = (Tensor(s, n, dt) for s in "xbty")
-    return (
-        Plan("scale+add, 2 kernels", (Kernel("t=x*a", (x,), (t,), n), Kernel("y=t+b", (t, b), (y,), n))),
-        Plan("scale+add, fused", (Kernel("y=x*a+b", (x, b), (y,), 2 * n),)),
-    )
+    v = nbytes(n, dt)  # one vector
+    # y = x * a + b: t = x * a, then y = t + b; fused, one launch
+    return (plan_cost("scale+add, 2 kernels", [(v, v, n), (2 * v, v, n)]),
+            plan_cost("scale+add, fused", [(2 * v, v, 2 * n)]))
 
 
 def _rmsnorm(m: int, n: int, dt: str):
-    x, w, y = Tensor("x", m * n, dt), Tensor("w", n, dt), Tensor("y", m * n, dt)
-    sq, sc = Tensor("x2", m * n, dt), Tensor("scaled", m * n, dt)
-    mean, mean_eps, rstd = (Tensor(s, m, "float32") for s in ("mean", "mean_eps", "rstd"))
-    steps = (
-        Kernel("x2=x*x", (x,), (sq,), m * n),
-        Kernel("mean=sum(x2)", (sq,), (mean,), m * n),
-        Kernel("+eps", (mean,), (mean_eps,), m),
-        Kernel("rsqrt", (mean_eps,), (rstd,), m),
-        Kernel("x*rstd", (x, rstd), (sc,), m * n),
-        Kernel("*w", (sc, w), (y,), m * n),
-    )
-    return Plan("RMSNorm, 6 eager steps", steps), Plan(
-        "RMSNorm, fused", (Kernel("rmsnorm", (x, w), (y,), 4 * m * n + 2 * m),)
-    )
+    big, row, wgt = nbytes(m * n, dt), nbytes(m, "float32"), nbytes(n, dt)
+    eager = [
+        (big, big, m * n),              # x * x
+        (big, row, m * n),              # row sums of the squares
+        (row, row, m),                  # + eps
+        (row, row, m),                  # rsqrt
+        (big + row, big, m * n),        # x * rstd
+        (big + wgt, big, m * n),        # * w
+    ]
+    return (plan_cost("RMSNorm, 6 eager steps", eager),
+            plan_cost("RMSNorm, fused", [(big + wgt, big, 4 * m * n + 2 * m)]))
 
 
 def _layernorm(m: int, n: int, dt: str):
-    x, g, b, y = Tensor("x", m * n, dt), Tensor("g", n, dt), Tensor("b", n, dt), Tensor("y", m * n, dt)
-    sq, acc = Tensor("x2", m * n, dt), Tensor("acc", m * n, dt)
-    sx, sx2 = Tensor("sum_x", m, "float32"), Tensor("sum_x2", m, "float32")
-    steps = (
-        Kernel("x2=x*x", (x,), (sq,), m * n),
-        Kernel("sum x", (x,), (sx,), m * n),
-        Kernel("sum x2", (sq,), (sx2,), m * n),
-        Kernel("x-mean", (x,), (acc,), m * n),
-        Kernel("*rstd", (acc,), (acc,), m * n),
-        Kernel("*g+b", (acc, g, b), (y,), 2 * m * n),
-    )
-    return Plan("LayerNorm, multi-pass", steps), Plan(
-        "LayerNorm, fused", (Kernel("layernorm", (x, g, b), (y,), 6 * m * n + 2 * m),)
-    )
+    big, row, vec = nbytes(m * n, dt), nbytes(m, "float32"), nbytes(n, dt)
+    passes = [
+        (big, big, m * n),              # x * x
+        (big, row, m * n),              # row sums of x
+        (big, row, m * n),              # row sums of x * x
+        (big, big, m * n),              # x - mean
+        (big, big, m * n),              # * rstd
+        (big + 2 * vec, big, 2 * m * n),  # * g + b
+    ]
+    return (plan_cost("LayerNorm, multi-pass", passes),
+            plan_cost("LayerNorm, fused", [(big + 2 * vec, big, 6 * m * n + 2 * m)]))
 
 
 def _rope(tokens: int, heads: int, rope_dim: int, dt: str):
     values = tokens * heads * rope_dim
-    pairs = values // 2
-    x, y = Tensor("x", values, dt), Tensor("y", values, dt)
-    rot, t, u = (Tensor(s, values, dt) for s in ("rot", "t", "u"))
-    cos_b, sin_b = Tensor("cos_b", values, dt), Tensor("sin_b", values, dt)
-    cos, sin = Tensor("cos", pairs, dt), Tensor("sin", pairs, dt)
-    steps = (
-        Kernel("rot=rotate_half(x)", (x,), (rot,), 0),
-        Kernel("t=x*cos", (x, cos_b), (t,), values),
-        Kernel("u=rot*sin", (rot, sin_b), (u,), values),
-        Kernel("y=t+u", (t, u), (y,), values),
-    )
-    return Plan("RoPE, 4 steps", steps), Plan("RoPE, fused", (Kernel("rope", (x, cos, sin), (y,), 3 * values),))
+    big, tab = nbytes(values, dt), nbytes(values // 2, dt)
+    steps = [
+        (big, big, 0),                  # rotate_half(x)
+        (2 * big, big, values),         # x * cos (broadcast to every value)
+        (2 * big, big, values),         # rotated * sin
+        (2 * big, big, values),         # sum
+    ]
+    return (plan_cost("RoPE, 4 steps", steps),
+            plan_cost("RoPE, fused", [(big + 2 * tab, big, 3 * values)]))
 
 
 def _norm_rope_quant(m: int, n: int, rope_dim: int, dt: str):
-    x, w = Tensor("x", m * n, dt), Tensor("w", n, dt)
-    cos, sin = Tensor("cos", m * rope_dim // 2, dt), Tensor("sin", m * rope_dim // 2, dt)
-    normed, rotated = Tensor("normed", m * n, dt), Tensor("rotated", m * n, dt)
-    q, amax = Tensor("q", m * n, "float8_e4m3fn"), Tensor("amax", m, "float32")
-    sep = (
-        Kernel("rmsnorm", (x, w), (normed,), 4 * m * n + 2 * m),
-        Kernel("rope", (normed, cos, sin), (rotated,), 3 * m * rope_dim),
-        Kernel("quant", (rotated,), (q, amax), 3 * m * n + m),
-    )
-    fused = Kernel("norm+rope+quant", (x, w, cos, sin), (q, amax), 4 * m * n + 3 * m * rope_dim + 3 * m * n + 3 * m)
-    return Plan("norm+rope+quant, 3 kernels", sep), Plan("norm+rope+quant, fused", (fused,))
+    big, wgt = nbytes(m * n, dt), nbytes(n, dt)
+    tab = 2 * nbytes(m * rope_dim // 2, dt)  # cos and sin
+    codes, amax = nbytes(m * n, "float8_e4m3fn"), nbytes(m, "float32")
+    f_norm, f_rope, f_quant = 4 * m * n + 2 * m, 3 * m * rope_dim, 3 * m * n + m
+    three = [
+        (big + wgt, big, f_norm),           # RMSNorm writes the normalised rows
+        (big + tab, big, f_rope),           # RoPE reads them back, writes the rotated rows
+        (big, codes + amax, f_quant),       # the quantiser reads those
+    ]
+    one = [(big + wgt + tab, codes + amax, f_norm + f_rope + f_quant)]
+    return plan_cost("norm+rope+quant, 3 kernels", three), plan_cost("norm+rope+quant, fused", one)
 
 
 def p4_plans():
-    """The chapter-13 ledger's five (unfused, fused) pairs at that page's default sizes."""
+    """The chapter-13 ledger's five (unfused, fused) plan pairs at that page's default sizes."""
     return [
         _scale_add(1 << 20, "float32"),
         _rmsnorm(4096, 4096, "float16"),

@@ -41,22 +41,24 @@ def test_p4_plan_pairs():
     g = GOLD["p4_ledger"]
     ais = []
     for (unf, fus), gp in zip(ledger.p4_plans(), g["pairs"]):
-        assert unf.moved == gp["unfused_moved"] and fus.moved == gp["fused_moved"]
-        assert unf.flops == gp["unfused_flops"] and fus.flops == gp["fused_flops"]
-        assert round(unf.moved / 1e6, 4) == gp["unfused_mb"]
-        assert round(fus.moved / 1e6, 4) == gp["fused_mb"]
-        assert round(unf.moved / fus.moved, 4) == gp["bytes_ratio"]
-        assert round(unf.ai, 6) == gp["unfused_ai"] and round(fus.ai, 6) == gp["fused_ai"]
-        assert fus.moved < unf.moved  # fusion always moves fewer bytes
-        ais += [unf.ai, fus.ai]
+        assert unf["moved"] == gp["unfused_moved"] and fus["moved"] == gp["fused_moved"]
+        assert unf["flops"] == gp["unfused_flops"] and fus["flops"] == gp["fused_flops"]
+        assert round(unf["moved"] / 1e6, 4) == gp["unfused_mb"]
+        assert round(fus["moved"] / 1e6, 4) == gp["fused_mb"]
+        assert round(unf["moved"] / fus["moved"], 4) == gp["bytes_ratio"]
+        assert round(unf["ai"], 6) == gp["unfused_ai"] and round(fus["ai"], 6) == gp["fused_ai"]
+        assert fus["moved"] < unf["moved"]  # fusion always moves fewer bytes
+        assert fus["kernels"] == 1 and unf["kernels"] > 1
+        ais += [unf["ai"], fus["ai"]]
     assert [round(min(ais), 3), round(max(ais), 3)] == g["ai_range_3dp"]
 
 
-def test_ledger_tensor_validation():
+def test_ledger_element_validation():
     with pytest.raises(ValueError):
-        ledger.Tensor("x", 4, "int3")
+        ledger.nbytes(4, "int3")
     with pytest.raises(ValueError):
-        ledger.Tensor("x", -1, "float32")
+        ledger.nbytes(-1, "float32")
+    assert ledger.nbytes(3, "bfloat16") == 6 and ledger.nbytes(3, "float8_e4m3fn") == 3
 
 
 def test_boundary_bytes_per_workload():
