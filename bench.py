@@ -326,6 +326,27 @@ def bench_rmsnorm(torch, rnq, workloads, ledger, name, steps, warmup):
     ]
 
 
+def bench_wide_norm_rope(torch, rnq, workloads, ledger, name, steps, warmup):
+    """Path R on rows wider than a head (the fusion page's check shape scaled to the
+    ledger page's plan: 4096 x 4096 bf16, rope 128, one table row per row)."""
+    return bench_norm_rope(torch, rnq, workloads, ledger, name, steps, warmup)
+
+
+ONLY_PATHS = {
+    "qk_4k": lambda t, r, w, l, s, wu: [bench_qk(t, r, w, l, "qk_4k", s, wu)],
+    "qk_small": lambda t, r, w, l, s, wu: [bench_qk(t, r, w, l, "qk_small", s, wu)],
+    "qk_4k_fused": lambda t, r, w, l, s, wu: [bench_qk(t, r, w, l, "qk_4k_fused", s, wu)],
+    "qk_64k": lambda t, r, w, l, s, wu: [bench_qk(t, r, w, l, "qk_64k", s, wu)],
+    "rmsnorm_4k": lambda t, r, w, l, s, wu: bench_rmsnorm(t, r, w, l, "rmsnorm_4k", s, wu),
+    "norm_rope_fp16": lambda t, r, w, l, s, wu: [bench_norm_rope(t, r, w, l, "norm_rope_fp16", s, wu)],
+    "norm_rope_pos": lambda t, r, w, l, s, wu: [bench_norm_rope(t, r, w, l, "norm_rope_pos", s, wu)],
+    "norm_rope_4k": lambda t, r, w, l, s, wu: [bench_wide_norm_rope(t, r, w, l, "norm_rope_4k", s, wu)],
+    "rope_bwd": lambda t, r, w, l, s, wu: [bench_rope_bwd(t, r, w, l, "norm_rope_fp16", s, wu)],
+    "rope_bwd_4k": lambda t, r, w, l, s, wu: [bench_rope_bwd(t, r, w, l, "norm_rope_4k", s, wu)],
+    "grouped_4k": lambda t, r, w, l, s, wu: [bench_grouped(t, r, w, l, "grouped_4k", s, wu)],
+}
+
+
 def _summary(r):
     gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
     out = {"workload": r["workload"], "us_per_call": round(r["ms"] * 1e3, 3), "GB/s": round(gbs, 1),
@@ -504,6 +525,9 @@ def main() -> int:
     ap.add_argument("--no-other-paths", action="store_true", help="time only the headline workload")
     ap.add_argument("--fusion-only", action="store_true",
                     help="time only the fused / unfused plan and the designs A/B/C; print their summary")
+    ap.add_argument("--only", default="",
+                    help="comma-separated paths to time alone, each with its same-run floor (one of: "
+                         + ", ".join(ONLY_PATHS) + "); prints their summaries")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 256 MiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
@@ -545,6 +569,16 @@ def main() -> int:
     if args.fusion_only:
         fpaths, fsum = bench_fusion(torch, rnq, workloads, ledger, args.steps, args.warmup)
         print(json.dumps({"fusion": fsum, "paths": [_summary(r) for r in fpaths]}), flush=True)
+        return 0
+    if args.only:
+        out = []
+        for name in args.only.split(","):
+            if name not in ONLY_PATHS:
+                print(f"bench.py: unknown path {name!r} (one of {', '.join(ONLY_PATHS)})", file=sys.stderr)
+                return 2
+            for r in ONLY_PATHS[name](torch, rnq, workloads, ledger, args.steps, args.warmup):
+                out.append(_with_floor(torch, _summary(r), args.steps, args.warmup))
+        print(json.dumps({"paths": out}), flush=True)
         return 0
     head = bench_qk(torch, rnq, workloads, ledger, args.workload, args.steps, args.warmup, hashes=True)
     wl = workloads.WORKLOADS[args.workload]
@@ -596,6 +630,8 @@ def main() -> int:
                                                                  steps, warm)), steps, warm))
         paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
         paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
+        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_4k", steps, warm)))
+        paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_4k", steps, warm)))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_4k_fused", steps, warm)))
         paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos",
                                                                  steps, warm)), steps, warm))

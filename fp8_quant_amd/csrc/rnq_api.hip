@@ -217,17 +217,42 @@ rnq_status rnq_rmsnorm_rope_ex(const void* x, int64_t x_token_stride, const void
   if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
   if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
   if (M % rows_per_token != 0) return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
-  if (!row_width_ok(N)) return fail(RNQ_ERR_UNSUPPORTED, "N must be 64, 128, 256 or 512 (got %lld)", (long long)N);
+  if (N % 8 != 0 || N > 16384)
+    return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
+  const bool narrow = row_width_ok(N);
+  if (!narrow && rope_dim > 1024)
+    return fail(RNQ_ERR_UNSUPPORTED, "rope_dim must be at most 1024 on rows other than 64..512 wide (got %lld)", (long long)rope_dim);
   if ((s = check_stride("x", x_token_stride, rows_per_token, N)) != RNQ_OK) return s;
   if ((s = check_positions(positions, table_rows, rope_dim)) != RNQ_OK) return s;
   if ((s = check_eps(eps)) != RNQ_OK) return s;
   if (M >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "M must stay below 2^31");
-  if (M == 0) return ok();
+  if (!narrow && (positions != nullptr ? table_rows : M / rows_per_token) * (rope_dim / 2) * 4 >= ((int64_t)1 << 31))
+    return fail(RNQ_ERR_UNSUPPORTED, "the cos/sin table must stay below 2 GiB");
+  if (M == 0 || N == 0) return ok();
   if (!x || !w || !y) return fail(RNQ_ERR_NULL, "x, w and y are required");
   if (rope_dim > 0 && (!cos || !sin)) return fail(RNQ_ERR_NULL, "cos and sin are required when rope_dim > 0");
   const void* a16[] = {x, w, y, cos, sin};
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
+
+  if (!narrow) {
+    // rows wider (or other) than a head: one workgroup per row
+    GroupQuantParams g = {};
+    g.x = (const uint16_t*)x;
+    g.xs = (uint64_t)x_token_stride;
+    g.w = (const uint16_t*)w;
+    g.cos = cos;
+    g.sin = sin;
+    g.positions = rope_dim > 0 ? positions : nullptr;
+    g.max_pos = (uint32_t)table_rows;
+    g.y = (uint16_t*)y;
+    g.M = (uint32_t)M;
+    g.N = (uint32_t)N;
+    g.rope = (uint32_t)rope_dim;
+    g.rows_per_token = (uint32_t)rows_per_token;
+    g.eps = eps;
+    return hip_status(launch_wide_norm_rope(g, dtype == RNQ_BF16, (hipStream_t)stream), "rnq_rmsnorm_rope");
+  }
 
   RowParams p = {};
   p.x0 = (const uint16_t*)x;
@@ -409,8 +434,8 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   if (M < 0 || N < 0) return fail(RNQ_ERR_SHAPE, "negative size (M %lld, N %lld)", (long long)M, (long long)N);
   if (N % 8 != 0 || N > 16384) return fail(RNQ_ERR_UNSUPPORTED, "N must be a multiple of 8 and at most 16384 (got %lld)", (long long)N);
   if ((s = check_rope(rope_dim, N)) != RNQ_OK) return s;
-  if (rope_dim > 0 && !narrow_bwd_width(N))
-    return fail(RNQ_ERR_UNSUPPORTED, "the RoPE backward takes rows of 64, 128, 256 or 512 (got %lld)", (long long)N);
+  if (rope_dim > 1024 && !narrow_bwd_width(N))
+    return fail(RNQ_ERR_UNSUPPORTED, "rope_dim must be at most 1024 on rows other than 64..512 wide (got %lld)", (long long)rope_dim);
   if (rows_per_token < 1) return fail(RNQ_ERR_SHAPE, "rows_per_token must be >= 1");
   if (M % rows_per_token != 0)
     return fail(RNQ_ERR_SHAPE, "M (%lld) is not a multiple of rows_per_token (%lld)", (long long)M, (long long)rows_per_token);
@@ -433,10 +458,10 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
   const uint32_t blocks = bwd_blocks(M, N);
   const uint32_t rows_per_block = (uint32_t)((M + blocks - 1) / blocks);
-  // the narrow kernel addresses a block's rows and the tables with 32-bit offsets
+  // the kernels address the tables (and the narrow one a block's rows) with 32-bit offsets
   const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;
-  if (narrow_bwd_width(N) &&
-      ((int64_t)rows_per_block * N * 2 >= ((int64_t)1 << 31) || table_bytes >= ((int64_t)1 << 31)))
+  if (table_bytes >= ((int64_t)1 << 31) ||
+      (narrow_bwd_width(N) && (int64_t)rows_per_block * N * 2 >= ((int64_t)1 << 31)))
     return fail(RNQ_ERR_UNSUPPORTED, "a block's rows or the cos/sin table exceed 2 GiB");
   if (use_scratch) {
     const rnq_status ss = scratch_for_stream((hipStream_t)stream, &workspace);
@@ -456,13 +481,12 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   p.blocks = blocks;
   p.rows_per_block = rows_per_block;
   p.eps = eps;
-  if (!narrow_bwd_width(N)) return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
-
   p.cos = cos;
   p.sin = sin;
   p.rope = (uint32_t)rope_dim;
   p.rows_per_token = (uint32_t)rows_per_token;
   p.table_bytes = (uint32_t)table_bytes;
+  if (!narrow_bwd_width(N)) return hip_status(launch_wide_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
   return hip_status(launch_narrow_bwd(p, dtype == RNQ_BF16, (hipStream_t)stream), name);
 }
 

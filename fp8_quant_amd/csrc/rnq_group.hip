@@ -15,6 +15,12 @@
 // the normalised tail goes through LDS (one barrier).
 // Every global access is a buffer access with a row-uniform descriptor (lanes
 // past the row's end use offsets outside its range).
+//
+// The same kernel without the quantiser (QUANT = false) is RMSNorm + RoPE
+// (the fusion page's rms_norm_rope_fused) over rows wider than a head: it
+// writes y only. Rows may sit in a token-strided view (x_token_stride
+// elements between the first rows of consecutive tokens) and the cos/sin row
+// of token t may be row positions[t] of a position-indexed table.
 #include "rnq_device.h"
 #include "rnq_launch.h"
 
@@ -24,7 +30,7 @@ constexpr int GT = 256;       // threads per workgroup
 constexpr int GWV = GT / 64;  // waves
 constexpr uint32_t kMaxRope = 1024;
 
-template <class DT, int KC, int GL>
+template <class DT, int KC, int GL, bool QUANT = true>
 __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   constexpr uint32_t kOutOfRange = 0x80000000u;
   __shared__ double part[GWV];
@@ -44,7 +50,17 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     ok[k] = ch[k] < nch;
     off[k] = ok[k] ? 16u * ch[k] : kOutOfRange;
   }
-  const rsrc_t rx = make_rsrc(p.x + (size_t)row * p.N, row_bytes);
+  // the row's token, its place in a (possibly strided) view, and its table row
+  const uint32_t tok = row / p.rows_per_token;
+  const size_t xoff = p.xs == 0 ? (size_t)row * p.N : (size_t)tok * p.xs + (size_t)(row - tok * p.rows_per_token) * p.N;
+  uint32_t trow = tok;
+  if (p.positions != nullptr) {
+    // a workgroup-uniform index read through the constant address space (a
+    // scalar load; the kernel never writes positions)
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    trow = min((uint32_t)((const_i32*)p.positions)[tok], p.max_pos - 1);
+  }
+  const rsrc_t rx = make_rsrc(p.x + xoff, row_bytes);
   const rsrc_t rw = make_rsrc(p.w, row_bytes);
   uint4 xr[KC], wr[KC];
 #pragma unroll
@@ -62,9 +78,10 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   for (int k = 0; k < KC; ++k)
     if (ok[k] && R > 0 && ch[k] >= t0) {
       const uint32_t j = ch[k] - t0;
-      toff = 4u * ((row / p.rows_per_token) * half + 8u * (j < hc ? j : j - hc));
+      toff = 4u * (trow * half + 8u * (j < hc ? j : j - hc));
     }
-  const uint32_t table_bytes = R > 0 ? ((p.M - 1) / p.rows_per_token + 1) * half * 4u : 0u;
+  const uint32_t table_rows = p.positions != nullptr ? p.max_pos : (p.M - 1) / p.rows_per_token + 1;
+  const uint32_t table_bytes = R > 0 ? table_rows * half * 4u : 0u;
   const rsrc_t rcos = make_rsrc(p.cos, table_bytes), rsin = make_rsrc(p.sin, table_bytes);
   const float4 tc0 = buf_load16f(rcos, toff), tc1 = buf_load16f(rcos, toff + 16u);
   const float4 ts0 = buf_load16f(rsin, toff), ts1 = buf_load16f(rsin, toff + 16u);
@@ -129,11 +146,12 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
       }
   }
 
-  if (p.y != nullptr) {
+  if (!QUANT || p.y != nullptr) {
     const rsrc_t ry = make_rsrc(p.y + (size_t)row * p.N, row_bytes);
 #pragma unroll
     for (int k = 0; k < KC; ++k) buf_store16_nt(ry, off[k], pack8<DT>(y[k]));
   }
+  if constexpr (!QUANT) return;
 
   // ---- per-group absmax, scale and codes
   const uint32_t n_groups = p.N / p.group_size;
@@ -221,6 +239,30 @@ static hipError_t launch_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
   if (nch <= 4 * GT) return launch_kc<DT, 4>(p, g, s);
   if (nch <= 8 * GT) return launch_kc<DT, 8>(p, g, s);
   return hipErrorInvalidValue;
+}
+
+template <class DT>
+static hipError_t launch_norm_rope_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
+  const uint32_t nch = p.N / 8;
+  if (nch <= GT)
+    hipLaunchKernelGGL((group_quant_kernel<DT, 1, 0, false>), g, dim3(GT), 0, s, p);
+  else if (nch <= 2 * GT)
+    hipLaunchKernelGGL((group_quant_kernel<DT, 2, 0, false>), g, dim3(GT), 0, s, p);
+  else if (nch <= 4 * GT)
+    hipLaunchKernelGGL((group_quant_kernel<DT, 4, 0, false>), g, dim3(GT), 0, s, p);
+  else if (nch <= 8 * GT)
+    hipLaunchKernelGGL((group_quant_kernel<DT, 8, 0, false>), g, dim3(GT), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_wide_norm_rope(GroupQuantParams p, bool bf16, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  if (p.rope > kMaxRope || p.y == nullptr || p.rows_per_token == 0) return hipErrorInvalidValue;
+  p.group_size = 0;
+  const dim3 grid(p.M);
+  return bf16 ? launch_norm_rope_dt<BF16>(p, grid, stream) : launch_norm_rope_dt<F16>(p, grid, stream);
 }
 
 hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream) {

@@ -84,7 +84,7 @@ struct WideBwdParams {
   uint32_t blocks;
   float eps;
   // the gradient goes back through the RoPE of the last `rope` columns first
-  // (narrow rows only; rope == 0: plain RMSNorm backward)
+  // (rope == 0: plain RMSNorm backward)
   const float* cos;  // [M / rows_per_token, rope / 2]
   const float* sin;
   uint32_t rope;
@@ -100,16 +100,19 @@ struct WideBwdParams {
 struct GroupQuantParams {
   const uint16_t* x;
   const uint16_t* w;
-  const float* cos;  // [M / rows_per_token, rope / 2]
+  const float* cos;  // [M / rows_per_token, rope / 2], or [max_pos, rope / 2] gathered through positions
   const float* sin;
-  uint16_t* y;       // optional
-  uint8_t* codes;    // [M, N]
-  float* scales;     // [M, N / group_size]
+  uint16_t* y;       // optional when quantising; the output of the no-quantise mode
+  uint8_t* codes;    // [M, N] (quantising mode)
+  float* scales;     // [M, N / group_size] (quantising mode)
+  const int32_t* positions;  // optional [M / rows_per_token]: table row of each token (clamped into range)
+  uint64_t xs;       // token stride of x in elements (0: contiguous rows)
+  uint32_t max_pos;  // table rows when positions are given
   uint32_t M;
   uint32_t N;
   uint32_t rope;
   uint32_t rows_per_token;
-  uint32_t group_size;
+  uint32_t group_size;  // 0: no quantisation (RMSNorm + RoPE into y only)
   float eps;
   float fp8_max;
   // filled by the launcher
@@ -120,6 +123,9 @@ struct GroupQuantParams {
 };
 
 hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream);
+// RMSNorm + RoPE (no quantisation) over rows of up to 16384 elements, one
+// workgroup per row (the grouped kernel's mode that writes y only)
+hipError_t launch_wide_norm_rope(GroupQuantParams p, bool bf16, hipStream_t stream);
 
 // row / d for every row < 2^31 as (row * magic) >> shift (64-bit product):
 // shift = 31 + lg with 2^lg >= d, magic = ceil(2^shift / d). With e = magic *
@@ -164,7 +170,7 @@ hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_
 
 // Deterministic row partition used by the backward (and its workspace size).
 uint32_t bwd_blocks(int64_t M, int64_t N);
-hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_wide_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
 // grad_w[j] = sum over b of partial[b, j] in a fixed order
 hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream);
 // rows of 64, 128, 256 or 512 elements, several per wave; rope optional

@@ -15,6 +15,14 @@
 // of rows and accumulates grad_y * xn for its columns in registers, in row
 // order; the per-workgroup partials go to the caller's workspace [blocks, N];
 // a second kernel adds them per column in a fixed order (dw_reduce_kernel).
+//
+// The backward of RMSNorm followed by the partial NeoX RoPE (chapter 13 fusion
+// page's rotation of the last R columns) first takes grad_y back through the
+// rotation: the transposed rotation (g_lo c + g_hi s, g_hi c - g_lo s) of each
+// pair p <-> p + R/2 of the tail, in fp32 (the casts to the input dtype count
+// as identities, as in the chapter 17 backward). A pair's two chunks belong to
+// different threads here, so each row's grad_y tail and its cos/sin row pass
+// through LDS, under the barrier the row sums take anyway.
 #include "rnq_device.h"
 #include "rnq_launch.h"
 
@@ -105,12 +113,20 @@ __global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
 // last row re-reads that row and writes its identical grad_x again, so no
 // access in the loop is conditional and the in-order memory counter is waited
 // on precisely. grad_w partials accumulate in ascending row order.
-template <class DT, int KC, int BT, int RB, bool SAVED>
+constexpr uint32_t kMaxBwdRope = 1024;
+
+template <class DT, int KC, int BT, int RB, bool SAVED, bool ROPE = false>
 __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   constexpr int BW = BT / 64;
   constexpr uint32_t kOutOfRange = 0x80000000u;
+  // table values a thread loads per row (cos then sin of the row's table row,
+  // R <= 1024 values in all)
+  constexpr int TPT = ROPE ? (int)((kMaxBwdRope + BT - 1) / BT) : 1;
   __shared__ double part_d[2][RB][BW];
   __shared__ float part_f[2][RB][BW];
+  // RoPE: each row's cos/sin values and its grad_y tail (16-bit values), by ring parity
+  __shared__ float tab_s[ROPE ? 2 : 1][RB][ROPE ? kMaxBwdRope : 1];
+  __shared__ uint4 gt_s[ROPE ? 2 : 1][RB][ROPE ? kMaxBwdRope / 8 : 1];
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = tid >> 6;
   const uint32_t nch = p.N / 8;
@@ -139,7 +155,22 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   };
   lds_barrier();
 
-  auto load_batch = [&](uint32_t first, uint4 (&xs)[RB][KC], uint4 (&gs)[RB][KC]) {
+  // RoPE geometry: R = p.rope columns at the end of the row, chunks t0 .. nch - 1,
+  // hc chunks per half; thread-owned table values e = tid + BT m (cos for e < R/2,
+  // then sin), out of the table's range past R
+  const uint32_t R = ROPE ? p.rope : 0u, half = R / 2;
+  const uint32_t t0 = nch - R / 8, hc = R / 16;
+  const rsrc_t rcos = make_rsrc(p.cos, ROPE ? p.table_bytes : 0u);
+  const rsrc_t rsin = make_rsrc(p.sin, ROPE ? p.table_bytes : 0u);
+  auto table_off = [&](uint32_t row, int m, bool& is_sin) {
+    const uint32_t e = tid + BT * m;
+    is_sin = e >= half;
+    if (e >= R) return kOutOfRange;
+    const uint32_t t = (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);
+    return 4u * (t * half + (is_sin ? e - half : e));
+  };
+
+  auto load_batch = [&](uint32_t first, uint4 (&xs)[RB][KC], uint4 (&gs)[RB][KC], float (&ts)[RB][TPT]) {
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const size_t row = min(first + (uint32_t)j, r1 - 1);
@@ -150,21 +181,46 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
         xs[j][k] = buf_load16_nt(rx, off[k]);
         gs[j][k] = buf_load16_nt(rg, off[k]);
       }
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+          bool is_sin;
+          const uint32_t o = table_off((uint32_t)row, m, is_sin);
+          // (both loads go out; the unused one is out of range and reads nothing)
+          const float c = buf_load4f(rcos, is_sin ? kOutOfRange : o);
+          const float sv = buf_load4f(rsin, is_sin ? o : kOutOfRange);
+          ts[j][m] = is_sin ? sv : c;
+        }
+      }
     }
   };
 
   uint4 xr[2][RB][KC], gr[2][RB][KC];
-  load_batch(r0, xr[0], gr[0]);
+  float tr[2][RB][TPT];
+  load_batch(r0, xr[0], gr[0], tr[0]);
   uint32_t parity = 0;
 
   // one batch; cur / nxt are compile-time ring slots
-  auto batch = [&](uint32_t first, uint4 (&xc)[RB][KC], uint4 (&gc)[RB][KC], uint4 (&xn_)[RB][KC],
-                   uint4 (&gn)[RB][KC]) {
-    load_batch(first + RB, xn_, gn);
+  auto batch = [&](uint32_t first, uint4 (&xc)[RB][KC], uint4 (&gc)[RB][KC], float (&tc)[RB][TPT],
+                   uint4 (&xn_)[RB][KC], uint4 (&gn)[RB][KC], float (&tn)[RB][TPT]) {
+    load_batch(first + RB, xn_, gn, tn);
+    if constexpr (ROPE) {
+      // this batch's table rows and grad_y tails into LDS (read after the next barrier)
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+#pragma unroll
+        for (int m = 0; m < TPT; ++m)
+          if (tid + BT * m < R) tab_s[parity][j][tid + BT * m] = tc[j][m];
+#pragma unroll
+        for (int k = 0; k < KC; ++k)
+          if (ok[k] && tid + BT * k >= t0) gt_s[parity][j][tid + BT * k - t0] = gc[j][k];
+      }
+    }
     float rstd[RB];
     if constexpr (SAVED) {
 #pragma unroll
       for (int j = 0; j < RB; ++j) rstd[j] = p.rstd[min(first + (uint32_t)j, r1 - 1)];
+      if constexpr (ROPE) lds_barrier();
     } else {
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
@@ -189,6 +245,41 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
       }
     }
 
+    // RoPE: grad_y through the transposed rotation on the tail (fp32), kept in registers
+    float gnr[ROPE ? RB : 1][ROPE ? KC : 1][8];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          unpack8<DT>(gc[j][k], gnr[j][k]);
+          const uint32_t c = tid + BT * k;
+          if (ok[k] && c >= t0) {
+            const uint32_t tj = c - t0;
+            const bool lo_half = tj < hc;
+            const uint32_t pj = lo_half ? tj : tj - hc;  // pair columns 8 pj .. 8 pj + 7 of the half
+            float pf[8];
+            unpack8<DT>(gt_s[parity][j][lo_half ? tj + hc : tj - hc], pf);
+            const float* cs = tab_s[parity][j] + 8 * pj;
+            const float* sn = tab_s[parity][j] + half + 8 * pj;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float own = gnr[j][k][i] * cs[i];
+              const float other = pf[i] * sn[i];
+              gnr[j][k][i] = lo_half ? own + other : own - other;
+            }
+          }
+        }
+    }
+    auto grad = [&](int j, int k, float* gf) {  // this lane's 8 output-gradient values of chunk k, row j
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gf[i] = gnr[j][k][i];
+      } else {
+        unpack8<DT>(gc[j][k], gf);
+      }
+    };
+
     // C = mean(g * xn): lane-sequential fp32 sum, wave butterfly, waves in ascending order
     float C[RB];
 #pragma unroll
@@ -198,7 +289,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
       for (int k = 0; k < KC; ++k) {
         float xf[8], gf[8], w[8];
         unpack8<DT>(xc[j][k], xf);
-        unpack8<DT>(gc[j][k], gf);
+        grad(j, k, gf);
         wk(k, w);
 #pragma unroll
         for (int i = 0; i < 8; ++i) dot += (gf[i] * w[i]) * (xf[i] * rstd[j]);
@@ -225,7 +316,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
       for (int k = 0; k < KC; ++k) {
         float xf[8], gf[8], o[8], w[8];
         unpack8<DT>(xc[j][k], xf);
-        unpack8<DT>(gc[j][k], gf);
+        grad(j, k, gf);
         wk(k, w);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -242,10 +333,10 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   const uint32_t nb = (r1 - r0 + RB - 1) / RB;
   uint32_t b = 0;
   for (; b + 2 <= nb; b += 2) {
-    batch(r0 + b * RB, xr[0], gr[0], xr[1], gr[1]);
-    batch(r0 + (b + 1) * RB, xr[1], gr[1], xr[0], gr[0]);
+    batch(r0 + b * RB, xr[0], gr[0], tr[0], xr[1], gr[1], tr[1]);
+    batch(r0 + (b + 1) * RB, xr[1], gr[1], tr[1], xr[0], gr[0], tr[0]);
   }
-  if (b < nb) batch(r0 + b * RB, xr[0], gr[0], xr[1], gr[1]);
+  if (b < nb) batch(r0 + b * RB, xr[0], gr[0], tr[0], xr[1], gr[1], tr[1]);
 
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
@@ -335,21 +426,32 @@ static hipError_t fwd_kc(const WideFwdParams& p, int kc, hipStream_t s) {
 #ifndef RNQ_BWD_BATCH
 #define RNQ_BWD_BATCH 2
 #endif
-template <class DT, bool SAVED>
+template <class DT, bool SAVED, bool ROPE>
 static hipError_t bwd_kc(const WideBwdParams& p, int kc, dim3 g, hipStream_t s) {
   constexpr int B = RNQ_BWD_BATCH;
   const size_t lds = 2 * (size_t)p.N;  // the weight row
   if (p.N <= 2048) {
-    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B, SAVED>), g, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B, SAVED, ROPE>), g, dim3(256), lds, s, p);
     return hipGetLastError();
   }
   switch (kc) {
-    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512, B, SAVED>), g, dim3(512), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512, (B > 2 ? B / 2 : 1), SAVED>), g, dim3(512), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512, (B > 4 ? B / 4 : 1), SAVED>), g, dim3(512), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 512, B, SAVED, ROPE>), g, dim3(512), lds, s, p); break;
+    case 2:
+      hipLaunchKernelGGL((wide_bwd_kernel<DT, 2, 512, (B > 2 ? B / 2 : 1), SAVED, ROPE>), g, dim3(512), lds, s, p);
+      break;
+    case 4:
+      hipLaunchKernelGGL((wide_bwd_kernel<DT, 4, 512, (B > 4 ? B / 4 : 1), SAVED, ROPE>), g, dim3(512), lds, s, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <class DT>
+static hipError_t bwd_dt(const WideBwdParams& p, int kc, dim3 g, hipStream_t s) {
+  const bool saved = p.rstd != nullptr, rope = p.rope > 0;
+  if (rope) return saved ? bwd_kc<DT, true, true>(p, kc, g, s) : bwd_kc<DT, false, true>(p, kc, g, s);
+  return saved ? bwd_kc<DT, true, false>(p, kc, g, s) : bwd_kc<DT, false, false>(p, kc, g, s);
 }
 
 static int chunks_per_lane(uint32_t N, uint32_t threads) {
@@ -375,12 +477,14 @@ uint32_t bwd_blocks(int64_t M, int64_t N) {
   return (uint32_t)((M + rpb - 1) / rpb);
 }
 
-hipError_t launch_wide_bwd(const WideBwdParams& p, bool bf16, hipStream_t stream) {
+hipError_t launch_wide_bwd(WideBwdParams p, bool bf16, hipStream_t stream) {
   dim3 grid(p.blocks);
   const int kc = chunks_per_lane(p.N, p.N > 2048 ? 512 : 256);
-  const bool saved = p.rstd != nullptr;
-  hipError_t e = bf16 ? (saved ? bwd_kc<BF16, true>(p, kc, grid, stream) : bwd_kc<BF16, false>(p, kc, grid, stream))
-                      : (saved ? bwd_kc<F16, true>(p, kc, grid, stream) : bwd_kc<F16, false>(p, kc, grid, stream));
+  if (p.rope > kMaxBwdRope || p.rope % 16 != 0 || p.rope > p.N) return hipErrorInvalidValue;
+  if (p.rows_per_token == 0) p.rows_per_token = 1;
+  // row / rows_per_token by multiply-shift (exact for every row < 2^31)
+  div_magic_for(p.rows_per_token, p.div_magic, p.div_shift);
+  hipError_t e = bf16 ? bwd_dt<BF16>(p, kc, grid, stream) : bwd_dt<F16>(p, kc, grid, stream);
   if (e != hipSuccess) return e;
   return launch_dw_reduce(p.partial, p.gw, p.blocks, p.N, stream);
 }

@@ -118,8 +118,10 @@ rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, con
  * x, y [M,N]; w [N]; cos, sin [M/rows_per_token, R/2] fp32; row m uses table
  * row t = m / rows_per_token (rows_per_token = heads per token for a
  * [tokens*heads, head_dim] layout; 1 for one table row per row).
- * Requirements: N in {64, 128, 256, 512}; R a multiple of 16 with R <= N;
- * M % rows_per_token == 0. cos/sin may be NULL when R == 0.
+ * Requirements: N a multiple of 8, at most 16384; R a multiple of 16 with
+ * R <= N, and R <= 1024 unless N is 64, 128, 256 or 512 (head-sized rows, the
+ * row kernel; other widths take one workgroup per row); M % rows_per_token == 0;
+ * the cos/sin table below 2 GiB. cos/sin may be NULL when R == 0.
  */
 rnq_status rnq_rmsnorm_rope(const void* x, const void* w, const float* cos, const float* sin,
                             void* y, int64_t M, int64_t N, int64_t rope_dim, int64_t rows_per_token,
@@ -152,9 +154,10 @@ rnq_status rnq_rmsnorm_rope_ex(const void* x, int64_t x_token_stride, const void
  * Layouts, rstd (NULL: recomputed), the workspace (rnq_rmsnorm_bwd_workspace_size(M, N)
  * bytes) and the fixed-order grad_w reduction are those of rnq_rmsnorm_bwd;
  * cos, sin and rows_per_token those of rnq_rmsnorm_rope.
- * Requirements: N in {64, 128, 256, 512} when rope_dim > 0 (any width
- * rnq_rmsnorm_bwd takes when rope_dim == 0); R a multiple of 16 with R <= N;
- * M % rows_per_token == 0. cos/sin may be NULL when R == 0.
+ * Requirements: N a multiple of 8, at most 16384 (the widths rnq_rmsnorm_bwd
+ * takes); R a multiple of 16 with R <= N, and R <= 1024 unless N is 64, 128,
+ * 256 or 512; M % rows_per_token == 0; the cos/sin table below 2 GiB. cos/sin
+ * may be NULL when R == 0.
  */
 rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y, const float* cos,
                                 const float* sin, const float* rstd, void* grad_x, float* grad_w,

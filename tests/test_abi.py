@@ -120,7 +120,10 @@ def test_rmsnorm_argument_validation():
     assert lib.rnq_rmsnorm_fwd(FAKE, FAKE, FAKE, None, -4, 4096, 1e-6, 0, None) == 2
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 128, 64, 4, 1e-6, 0, None) == 2
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 128, 64, 1, 1e-6, 0, None) == 1
-    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 3
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4100, 64, 1, 1e-6, 0, None) == 3  # not whole chunks
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 16392, 64, 1, 1e-6, 0, None) == 3  # too wide
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 2048, 1, 1e-6, 0, None) == 3  # tail > 1024
+    assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 1  # wide rows, no table
     need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 4096)
     assert need == 512 * 4096 * 4  # 512 blocks of 8 rows
     assert lib.rnq_rmsnorm_bwd_workspace_size(16384, 4096) == 256 * 4096 * 4
@@ -188,7 +191,7 @@ def test_rope_bwd_argument_validation():
     assert call(x=None) == 1
     assert call(cos=None) == 1
     assert call(M=0, x=None) == 0
-    assert call(N=1024, R=64) == 3  # the RoPE backward takes narrow rows only
+    assert call(N=4096, R=2048) == 3  # tails above 1024 only on rows of 64..512
     assert call(N=4100, R=0) == 3
     assert call(R=24) == 3
     assert call(R=63) == 2
@@ -213,7 +216,7 @@ def test_noalloc_bwd_argument_validation():
     assert call(x=None) == 1
     assert call(cos=None) == 1
     assert call(M=0, x=None) == 0
-    assert call(N=1024, R=64) == 3
+    assert call(N=4096, R=2048) == 3
     assert call(N=16392, R=0) == 3  # wider than any row the backward takes
     assert call(R=24) == 3
     assert call(R=63) == 2
@@ -267,7 +270,7 @@ def test_strided_entry_validation():
     assert nr(xs=4 * 128 + 12) == 3
     assert nr(pos=P, rows=-1) == 2
     assert nr(M=62) == 2
-    assert nr(N=1024) == 3
+    assert nr(N=4096, R=2048) == 3  # wide rows take tails up to 1024
     assert nr(M=0) == 0
 
 

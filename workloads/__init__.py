@@ -25,6 +25,8 @@ where M = tokens x heads, weight ``[N]``, cos/sin ``[tokens, rope_dim/2]``):
   the random positions from a [8192, 32] table instead of one table row per row
 * ``nrq_4k`` - the chapter 13 ledger page's norm+rope+quant plan size: 4096 x 4096
   bf16, rope 128, one FP8 scale per row (fused, or as three kernels)
+* ``norm_rope_4k`` - RMSNorm + partial RoPE (no quant) on rows wider than a head:
+  4096 x 4096 bf16, rope 128, one cos/sin row per row (pos = row)
 """
 
 from __future__ import annotations
@@ -118,6 +120,10 @@ WORKLOADS: dict[str, Workload] = {
         Workload(
             "nrq_4k", "grouped", seed=1010, rows=4096, width=4096, rope_dim=128, group_size=4096,
             description="RMSNorm + RoPE + per-row FP8 on 4096 x 4096 bf16 rows, rope 128 (the ledger page's plan)",
+        ),
+        Workload(
+            "norm_rope_4k", "norm_rope", seed=1011, rows=4096, width=4096, rope_dim=128,
+            description="RMSNorm + partial RoPE (no quant), 4096 x 4096 bf16 rows, rope 128",
         ),
         Workload(
             "norm_rope_pos", "norm_rope", seed=1009, rows=16384, width=128, rope_dim=64,
