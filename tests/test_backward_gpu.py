@@ -179,3 +179,51 @@ def test_autograd_only_weight_grad():
                                            cos.numpy(), sin.numpy(), 1e-6, "bf16", 1)
     dw = wg.grad.float().cpu().numpy()
     assert np.abs(dw - ref_dw).max() <= 2e-2 * (np.abs(ref_dw).max() + 1e-30)
+
+
+# ------------------------------------------- grad_w: every row counted exactly once
+
+EDGE = [
+    # M, N, R, dtype, rows_per_token
+    (4096, 4096, 0, torch.bfloat16, 1),     # wide rows: 512 blocks of 8 rows
+    (4100, 2048, 0, torch.bfloat16, 1),     # ragged: 456 blocks of 9 rows, the last one of 5
+    (16384, 128, 0, torch.float16, 1),      # narrow rows: 512 blocks of 32
+    (16384, 128, 64, torch.float16, 1),     # narrow rows through the RoPE backward
+    (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward
+    (20000, 256, 0, torch.bfloat16, 1),     # above 8192 rows: 256 blocks
+]
+
+
+@pytest.mark.parametrize("M,N,R,dtype,rpt", EDGE, ids=[f"{m}x{n}r{r}" for m, n, r, _, _ in EDGE])
+def test_grad_w_counts_block_edge_rows_once(M, N, R, dtype, rpt):
+    """grad_y is nonzero only on the first and last rows of a few of the fixed
+    row blocks (the first, one in the middle, the last) and on row M - 1: a row
+    dropped from, or counted twice in, the block partition or the fixed-order
+    reduction moves a column of grad_w by a whole row's gy * xn, which the
+    per-column bound 1e-4 * sum over rows of |gy * xn| catches (the 2e-2 rule
+    of the full-size tests cannot see one row out of thousands)."""
+    blocks = rnq.rnq_rmsnorm_bwd_workspace_size(M, N) // (4 * N)
+    rpb = -(-M // blocks)
+    picks = sorted({r for b in (0, blocks // 2, blocks - 1) for r in (b * rpb, min(b * rpb + rpb, M) - 1)} | {M - 1})
+    print(f"[bwd] grad_w edge rows M{M} N{N} R{R}: {blocks} blocks of {rpb}, rows {picks}", flush=True)
+    x, w, gy, cos, sin = _case(M, N, R, seed=M + N + R, dtype=dtype, rows_per_token=rpt)
+    mask = torch.zeros(M, 1, dtype=torch.bool)
+    mask[picks] = True
+    gy = torch.where(mask, gy, torch.zeros_like(gy))
+    if R:
+        _, gw = rnq.rmsnorm_rope_bwd(gpu(x), gpu(w), gpu(gy), gpu(cos), gpu(sin), rows_per_token=rpt)
+    else:
+        _, gw = rnq.rmsnorm_bwd(gpu(x), gpu(w), gpu(gy))
+    torch.cuda.synchronize()
+    xb, wb, gb = workloads.bits(x), workloads.bits(w), workloads.bits(gy)
+    dt = DT[dtype]
+    ref_dx, ref_dw, rstd = oracle.rmsnorm_rope_bwd(xb, wb, gb, cos.numpy(), sin.numpy(), 1e-6, dt, rpt)
+    # sum over rows of |gn * xn| per column (gn: grad_y through the transposed rotation)
+    xn = codecs.dtype_to_f32(xb, dt).astype(np.float64) * rstd[:, None]
+    t = np.arange(M) // rpt
+    gn = oracle.rope_bwd_rotate(codecs.dtype_to_f32(gb, dt).astype(np.float64), cos.numpy()[t], sin.numpy()[t])
+    mag = np.abs(gn * xn).sum(axis=0)
+    err = np.abs(gw.cpu().numpy().astype(np.float64) - ref_dw)
+    worst = (err / np.maximum(mag, 1e-30)).max()
+    print(f"[bwd] grad_w edge rows: worst |dw - ref| / sum|gy xn| = {worst:.3g}", flush=True)
+    assert np.all(err <= 1e-4 * mag + 1e-30)

@@ -73,26 +73,41 @@ def test_qk_4k_full_size():
     assert np.array_equal(got_y["q_codes"], got["q_codes"])
 
 
-def test_qk_64k_sampled_rows():
-    """65536 tokens x (64 + 8) heads x 128: every head of the first and last token and
-    65536 seeded random rows, each checked against the oracle."""
+@pytest.fixture(scope="module")
+def qk_64k_run():
+    """The 65536-token workload (64 + 8 heads x 128, 1.2 GB of input) through the GPU once."""
     d = workloads.generate("qk_64k")
     print("[parity] qk_64k generated", flush=True)
     got = run_qk_gpu(d, with_y=False)
-    T, Hq, D = d["q"].shape
-    Hk = d["k"].shape[1]
-    rng = np.random.default_rng(2024)
-    for part, H in (("q", Hq), ("k", Hk)):
-        rows = np.unique(np.concatenate([
-            np.arange(H), (T - 1) * H + np.arange(H), rng.integers(0, T * H, 32768)]))
-        toks, heads = rows // H, rows % H
-        xb = workloads.bits(d[part]).reshape(T * H, D)[rows]
-        wb = workloads.bits(d["w" + part])
-        c, s = d["cos"].numpy()[toks], d["sin"].numpy()[toks]
-        y, codes, scale = oracle.norm_rope_quant_rows(xb, wb, c, s, 1e-6, 448.0)
-        gc = got[part + "_codes"].reshape(T * H, D)[rows]
-        gs = got[part + "_scale"].reshape(T * H)[rows]
-        assert_rows_match(f"qk_64k/{part}", None, gc, gs, None, codes, scale, unproven_rows(xb, "bf16"))
+    print("[parity] qk_64k ran on the GPU", flush=True)
+    return d, got
+
+
+def _oracle_chunk(d, got, part, lo, hi):
+    """Compare tokens [lo, hi) of one tensor with the oracle, row by row."""
+    T, H, D = d[part].shape
+    xb = workloads.bits(d[part])[lo:hi]
+    wb = workloads.bits(d["w" + part])
+    toks = np.repeat(np.arange(lo, hi), H)
+    c, s = d["cos"].numpy()[toks], d["sin"].numpy()[toks]
+    rows = xb.reshape(-1, D)
+    y, codes, scale = oracle.norm_rope_quant_rows(rows, wb, c, s, 1e-6, 448.0)
+    assert_rows_match(f"qk_64k/{part} tokens {lo}..{hi}", None, got[part + "_codes"][lo:hi].reshape(-1, D),
+                      got[part + "_scale"][lo:hi].reshape(-1), None, codes, scale, unproven_rows(rows, "bf16"))
+    return rows.shape[0]
+
+
+@pytest.mark.parametrize("quarter", [0, 1, 2, 3])
+def test_qk_64k_every_row(qk_64k_run, quarter):
+    """65536 tokens x (64 + 8) heads x 128, every row of a quarter of the tokens
+    (the four cases cover the whole workload), against the oracle in 1024-token
+    chunks (about 10 s of oracle time per quarter)."""
+    d, got = qk_64k_run
+    T = d["q"].shape[0]
+    lo, hi = quarter * T // 4, (quarter + 1) * T // 4
+    done = sum(_oracle_chunk(d, got, part, a, min(a + 1024, hi)) for part in ("q", "k") for a in range(lo, hi, 1024))
+    print(f"[parity] qk_64k tokens {lo}..{hi}: {done} rows checked", flush=True)
+    assert done == (hi - lo) * (d["q"].shape[1] + d["k"].shape[1])
 
 
 def test_norm_rope_fp16_full_size():
