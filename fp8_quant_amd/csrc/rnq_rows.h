@@ -30,7 +30,13 @@
 //  * When every pass stays inside one token and one tensor (heads and q heads
 //    both multiples of G, the usual QK layout), a pass's token and tensor are
 //    wave-uniform and its addresses are one scalar base plus lane-constant
-//    offsets. Otherwise each lane locates its own row.
+//    offsets. When instead every pass holds whole tokens of one tensor (G a
+//    multiple of the heads per token: one row per token of path R, the
+//    RMSNorm forward, a single-tensor prologue), the same holds with the
+//    pass's first token as the base: the rows of its G / heads tokens sit at
+//    lane-constant offsets, and their table rows are one contiguous block
+//    (16 bytes per lane, staged through LDS like a token's row). Otherwise each
+//    lane locates its own row.
 //  * Inputs may be views: the rows of a token are contiguous in each input
 //    tensor, and consecutive tokens are xs0 / xs1 elements apart (q and k
 //    inside a fused QKV projection output). Outputs are contiguous.
@@ -100,10 +106,21 @@ __device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) 
   return (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);  // row / heads, exact below 2^31
 }
 
-template <int G, int D, bool ALIGNED, bool POS>
+template <int G, int D, bool ALIGNED, bool POS, bool MT>
 __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_t slot) {
   Loc r;
-  if constexpr (ALIGNED) {
+  if constexpr (MT) {
+    // whole tokens of tensor 0: the pass's first row and token are wave-uniform
+    static_assert(ALIGNED && !POS, "several tokens per pass: aligned, table rows read in order");
+    const uint32_t row0 = __builtin_amdgcn_readfirstlane(pass * (uint32_t)G);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(row0 >> p.tok_shift);
+    r.second = false;
+    r.tok = t;
+    r.ri0 = row0;
+    r.ri = row0 + slot;
+    r.row = row0 + slot;
+    r.xoff = (uint64_t)t * p.xs0;
+  } else if constexpr (ALIGNED) {
     // the whole pass lies inside one token and one tensor, and the launch
     // holds whole passes only: everything but the slot is wave-uniform
     // (readfirstlane: keep the wave-uniform values in scalar registers through
@@ -150,7 +167,7 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
   return r;
 }
 
-template <class DT, int L, int MODE, bool ALIGNED>
+template <class DT, int L, int MODE, bool ALIGNED, bool MT = false>
 __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr bool QUANT = (MODE & ROW_QUANT) != 0;
   constexpr bool ROPE = (MODE & ROW_ROPE) != 0;
@@ -161,8 +178,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr int G = 64 / L;
   __shared__ float w_lds[2 * D];
   // aligned rope passes: each wave stages the pass's cos and sin rows here
+  // (several tokens' rows, at most 1 KB of each, when a pass holds whole tokens)
   constexpr bool STAGED = ALIGNED && ROPE;
-  __shared__ float t_lds[STAGED ? RW * D : 1];
+  constexpr int TW = MT ? (D > 512 ? D : 512) : D;  // floats per wave
+  __shared__ float t_lds[STAGED ? RW * TW : 1];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -202,18 +221,26 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     cs_off = 8 * j;
   }
   // aligned passes: element offsets of this lane's chunks from the pass's first row
+  // (outputs: contiguous rows; inputs: tokens xs0 elements apart when a pass holds
+  // several tokens, the row's place inside its token otherwise)
   const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
+  uint32_t px0 = slot * D;
+  if constexpr (MT) px0 = (slot >> p.tok_shift) * (uint32_t)p.xs0 + (slot & ((1u << p.tok_shift) - 1u)) * D;
+  const uint32_t px_a = px0 + off_a, px_b = px0 + off_b;
   // aligned rope passes: lane l carries bytes [TB l, TB l + TB) of the token's
   // cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB bytes
   // cover it, each byte read once; lanes past the row read zero)
-  constexpr uint32_t TB = D / 32 < 4 ? 4u : (uint32_t)(D / 32);
+  constexpr uint32_t TB = MT ? 16u : (D / 32 < 4 ? 4u : (uint32_t)(D / 32));
   const uint32_t toff = TB * lane;
-  const bool t_lane = toff < 4u * half;
-  float* t_wave = t_lds + (STAGED ? wave * D : 0);
+  // the pass's table block: one row, or the rows of its tokens in order
+  const uint32_t tpp = MT ? (uint32_t)G >> p.tok_shift : 1u;  // tokens per pass
+  const uint32_t tbytes = 4u * half * tpp;                      // bytes of the block (cos or sin)
+  const bool t_lane = toff < tbytes;
+  float* t_wave = t_lds + (STAGED ? wave * TW : 0);
 
   auto load_staged_table = [&](Data& d) {
-    const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, 4u * half);
-    const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, 4u * half);
+    const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, tbytes);
+    const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, tbytes);
     if constexpr (TB == 4) {
       d.cw.x = buf_load4(rc, toff);
       d.sw.x = buf_load4(rs, toff);
@@ -226,12 +253,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     }
   };
   auto load_data = [&](Data& d, uint32_t pass) {
-    d.loc = locate<G, D, ALIGNED, POS>(p, pass, slot);
+    d.loc = locate<G, D, ALIGNED, POS, MT>(p, pass, slot);
     if constexpr (ALIGNED) {
       // the pass's G rows: one wave-uniform descriptor, lane byte offsets
-      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, 2u * G * D);
-      d.xa = buf_load16_nt(rx, 2u * pe_a);
-      d.xb = buf_load16_nt(rx, 2u * pe_b);
+      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, MT ? p.xspan : 2u * G * D);
+      d.xa = buf_load16_nt(rx, 2u * px_a);
+      d.xb = buf_load16_nt(rx, 2u * px_b);
       // the token's cos and sin rows (wave-uniform descriptors), one chunk of
       // each per lane, in flight with the input: the wait for a pass's input
       // covers them, and it never waits on the previous pass's stores. (With a
@@ -300,16 +327,18 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
       // accesses complete in order, so the reads below see these writes and the
       // previous pass's reads are done before they land
+      // (cos block, then sin block: tpp * half floats each)
+      const uint32_t sin_at = tpp * half;
       if (t_lane) {
         if constexpr (TB == 4) {
           t_wave[lane] = __uint_as_float(s.cw.x);
-          t_wave[half + lane] = __uint_as_float(s.sw.x);
+          t_wave[sin_at + lane] = __uint_as_float(s.sw.x);
         } else if constexpr (TB == 8) {
           *(uint2*)(t_wave + 2 * lane) = make_uint2(s.cw.x, s.cw.y);
-          *(uint2*)(t_wave + half + 2 * lane) = make_uint2(s.sw.x, s.sw.y);
+          *(uint2*)(t_wave + sin_at + 2 * lane) = make_uint2(s.sw.x, s.sw.y);
         } else {
           *(uint4*)(t_wave + 4 * lane) = s.cw;
-          *(uint4*)(t_wave + half + 4 * lane) = s.sw;
+          *(uint4*)(t_wave + sin_at + 4 * lane) = s.sw;
         }
       }
     }
@@ -319,10 +348,13 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       if (FULL || rope_lane) {
         float4 c0 = t.c0, c1 = t.c1, s0 = t.s0, s1 = t.s1;
         if constexpr (STAGED) {
-          c0 = *(const float4*)(t_wave + cs_off);
-          c1 = *(const float4*)(t_wave + cs_off + 4);
-          s0 = *(const float4*)(t_wave + half + cs_off);
-          s1 = *(const float4*)(t_wave + half + cs_off + 4);
+          // this row's token inside the pass (0 unless a pass holds several tokens)
+          const uint32_t tb = MT ? (slot >> p.tok_shift) * half : 0u;
+          const uint32_t sb = tpp * half + tb;
+          c0 = *(const float4*)(t_wave + tb + cs_off);
+          c1 = *(const float4*)(t_wave + tb + cs_off + 4);
+          s0 = *(const float4*)(t_wave + sb + cs_off);
+          s1 = *(const float4*)(t_wave + sb + cs_off + 4);
         }
         const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -447,6 +479,22 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   __syncthreads();
   if (gw >= W) return;
 
+  // Issue priority by progress (launches whose waves are all resident at once):
+  // a SIMD's arbiter favours its oldest wave, so the four waves of a SIMD would
+  // otherwise finish one after another, the last ones alone on a SIMD whose
+  // memory traffic has stopped. Each wave starts at the highest priority and
+  // steps down as its share of passes done grows (quarters of n), so waves
+  // that are behind issue first and a SIMD's waves finish together.
+  const bool by_progress = p.prio_by_progress != 0;
+  if (by_progress) __builtin_amdgcn_s_setprio(3);
+  auto progress = [&](uint32_t done) {
+    if (!by_progress) return;
+    const uint32_t q = (4u * done) / n;
+    if (q >= 3) __builtin_amdgcn_s_setprio(0);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  };
+
   auto run = [&](auto opts) {
     uint32_t base = 0;
     for (; base + NS <= n; base += NS) {
@@ -459,6 +507,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
           load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
           compute(d[k], tb[k % 2], d[k], opts);
         }
+        progress(base + k + 1);
       }
     }
     // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
@@ -490,7 +539,11 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     run(Opts<false, false>{});
 }
 
+// How a launch's passes sit in the rows: each lane locates its own row, a
+// pass inside one token of one tensor, or a pass of whole tokens of one tensor.
+enum RowsAlign : int { ROWS_PER_LANE = 0, ROWS_ONE_TOKEN = 1, ROWS_WHOLE_TOKENS = 2 };
+
 template <int MODE>
-hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, bool aligned, dim3 grid, hipStream_t s);
+hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, int align, dim3 grid, hipStream_t s);
 
 }  // namespace rnq

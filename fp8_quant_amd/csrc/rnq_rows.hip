@@ -8,6 +8,9 @@ namespace rnq {
 #ifndef RNQ_ROWS_TARGET_WAVES
 #define RNQ_ROWS_TARGET_WAVES 4096  // 4 per SIMD: what stays resident at the kernel's register use
 #endif
+#ifndef RNQ_ROWS_PRIO
+#define RNQ_ROWS_PRIO 1  // issue priority by progress: 0 never, 1 when every wave is resident at once, 2 always
+#endif
 #ifndef RNQ_ROWS_MAX_PER_WAVE
 #define RNQ_ROWS_MAX_PER_WAVE 8  // larger launches: more waves, dispatched in order as others retire
 #endif
@@ -20,7 +23,7 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   div_magic_for(p.heads, p.div_magic, p.div_shift);
   // passes stay inside one token and one tensor when both head counts are
   // multiples of G (then total_rows is a multiple of G too: whole passes only)
-  const bool aligned = p.heads % G == 0 && p.heads0 % G == 0;
+  int align = p.heads % G == 0 && p.heads0 % G == 0 ? ROWS_ONE_TOKEN : ROWS_PER_LANE;
   // the same number of passes for every wave: as few waves as keep the
   // SIMDs busy, at most RNQ_ROWS_MAX_PER_WAVE passes each. Waves that do not
   // fit at once start as others retire, in launch order, so the active
@@ -28,6 +31,10 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.per_wave = (p.passes + RNQ_ROWS_TARGET_WAVES - 1) / RNQ_ROWS_TARGET_WAVES;
   if (p.per_wave > RNQ_ROWS_MAX_PER_WAVE) p.per_wave = RNQ_ROWS_MAX_PER_WAVE;
   p.waves = (p.passes + p.per_wave - 1) / p.per_wave;
+  // (more waves than stay resident start as earlier ones retire, oldest first:
+  // progress priority only where they all run at once)
+  p.prio_by_progress = RNQ_ROWS_PRIO == 2 || (RNQ_ROWS_PRIO == 1 && p.per_wave > 1 && p.waves <= RNQ_ROWS_TARGET_WAVES)
+                           ? 1u : 0u;
   const dim3 grid((p.waves + RW - 1) / RW);
   // scale = RN(max(amax, 1e-4) / fp8_max) through the reciprocal of fp8_max
   // when fp8_max >= 1 (no overflow for any 16-bit amax)
@@ -41,23 +48,38 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   if (p.xs0 == 0) p.xs0 = (uint64_t)p.heads0 * (uint64_t)head_dim;
   if (p.xs1 == 0) p.xs1 = (uint64_t)(p.heads - p.heads0) * (uint64_t)head_dim;
   const bool pos = p.rope > 0 && p.positions != nullptr;
+  // passes of whole tokens of one tensor (G a multiple of the heads per token,
+  // whole passes only, table rows read in order): the tokens of a pass sit at
+  // lane-constant offsets and their table rows form one block of at most 1 KB
+  // per table (16 bytes per lane)
+  if (align == ROWS_PER_LANE && !pos && p.heads0 == p.heads && G % p.heads == 0 && p.total_rows % G == 0) {
+    uint32_t sh = 0;
+    while ((1u << sh) < p.heads) ++sh;
+    const uint64_t tpp = G >> sh;
+    const uint64_t span = 2 * ((tpp - 1) * p.xs0 + (uint64_t)p.heads * (uint64_t)head_dim);
+    if (span < ((uint64_t)1 << 31) && tpp * (p.rope / 2) * 4 <= 1024) {
+      align = ROWS_WHOLE_TOKENS;
+      p.tok_shift = sh;
+      p.xspan = (uint32_t)span;
+    }
+  }
   const int mode = (quant ? ROW_QUANT : 0) | (p.rope > 0 ? ROW_ROPE : 0) | (p.y0 != nullptr ? ROW_Y : 0) |
                    (p.rstd != nullptr ? ROW_RSTD : 0) | (pos ? ROW_POS : 0);
   switch (mode) {
-    case ROW_QUANT: return launch_rows_mode<ROW_QUANT>(p, head_dim, bf16, aligned, grid, stream);
-    case ROW_QUANT | ROW_ROPE: return launch_rows_mode<ROW_QUANT | ROW_ROPE>(p, head_dim, bf16, aligned, grid, stream);
-    case ROW_QUANT | ROW_Y: return launch_rows_mode<ROW_QUANT | ROW_Y>(p, head_dim, bf16, aligned, grid, stream);
+    case ROW_QUANT: return launch_rows_mode<ROW_QUANT>(p, head_dim, bf16, align, grid, stream);
+    case ROW_QUANT | ROW_ROPE: return launch_rows_mode<ROW_QUANT | ROW_ROPE>(p, head_dim, bf16, align, grid, stream);
+    case ROW_QUANT | ROW_Y: return launch_rows_mode<ROW_QUANT | ROW_Y>(p, head_dim, bf16, align, grid, stream);
     case ROW_QUANT | ROW_ROPE | ROW_Y:
-      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y>(p, head_dim, bf16, aligned, grid, stream);
-    case ROW_Y: return launch_rows_mode<ROW_Y>(p, head_dim, bf16, aligned, grid, stream);
-    case ROW_Y | ROW_ROPE: return launch_rows_mode<ROW_Y | ROW_ROPE>(p, head_dim, bf16, aligned, grid, stream);
-    case ROW_Y | ROW_RSTD: return launch_rows_mode<ROW_Y | ROW_RSTD>(p, head_dim, bf16, aligned, grid, stream);
+      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y>(p, head_dim, bf16, align, grid, stream);
+    case ROW_Y: return launch_rows_mode<ROW_Y>(p, head_dim, bf16, align, grid, stream);
+    case ROW_Y | ROW_ROPE: return launch_rows_mode<ROW_Y | ROW_ROPE>(p, head_dim, bf16, align, grid, stream);
+    case ROW_Y | ROW_RSTD: return launch_rows_mode<ROW_Y | ROW_RSTD>(p, head_dim, bf16, align, grid, stream);
     case ROW_QUANT | ROW_ROPE | ROW_POS:
-      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
+      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_POS>(p, head_dim, bf16, align, grid, stream);
     case ROW_QUANT | ROW_ROPE | ROW_Y | ROW_POS:
-      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
+      return launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y | ROW_POS>(p, head_dim, bf16, align, grid, stream);
     case ROW_Y | ROW_ROPE | ROW_POS:
-      return launch_rows_mode<ROW_Y | ROW_ROPE | ROW_POS>(p, head_dim, bf16, aligned, grid, stream);
+      return launch_rows_mode<ROW_Y | ROW_ROPE | ROW_POS>(p, head_dim, bf16, align, grid, stream);
     default: return hipErrorInvalidValue;  // not a combination the entry points produce
   }
 }

@@ -7,11 +7,19 @@
 namespace rnq {
 
 template <class DT, int L, int MODE>
-static hipError_t launch_shape(const RowParams& p, bool aligned, dim3 grid, hipStream_t s) {
-  if (aligned)
+static hipError_t launch_shape(const RowParams& p, int align, dim3 grid, hipStream_t s) {
+  if constexpr ((MODE & ROW_POS) == 0) {
+    if (align == ROWS_WHOLE_TOKENS) {
+      hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true, true>), grid, dim3(RT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (align == ROWS_ONE_TOKEN)
     hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true>), grid, dim3(RT), 0, s, p);
-  else
+  else if (align == ROWS_PER_LANE)
     hipLaunchKernelGGL((rows_kernel<DT, L, MODE, false>), grid, dim3(RT), 0, s, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -20,20 +28,20 @@ static hipError_t launch_shape(const RowParams& p, bool aligned, dim3 grid, hipS
 // and each code store whole 128-byte rows (64-byte halves where the rope tail
 // does not allow the lane-pair swap).
 template <class DT, int MODE>
-static hipError_t launch_dt(const RowParams& p, int D, bool aligned, dim3 grid, hipStream_t s) {
+static hipError_t launch_dt(const RowParams& p, int D, int align, dim3 grid, hipStream_t s) {
   switch (D) {
-    case 64: return launch_shape<DT, 4, MODE>(p, aligned, grid, s);
-    case 128: return launch_shape<DT, 8, MODE>(p, aligned, grid, s);
-    case 256: return launch_shape<DT, 16, MODE>(p, aligned, grid, s);
-    case 512: return launch_shape<DT, 32, MODE>(p, aligned, grid, s);
+    case 64: return launch_shape<DT, 4, MODE>(p, align, grid, s);
+    case 128: return launch_shape<DT, 8, MODE>(p, align, grid, s);
+    case 256: return launch_shape<DT, 16, MODE>(p, align, grid, s);
+    case 512: return launch_shape<DT, 32, MODE>(p, align, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int MODE>
-hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, bool aligned, dim3 grid, hipStream_t s) {
-  return bf16 ? launch_dt<BF16, MODE>(p, head_dim, aligned, grid, s)
-              : launch_dt<F16, MODE>(p, head_dim, aligned, grid, s);
+hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, int align, dim3 grid, hipStream_t s) {
+  return bf16 ? launch_dt<BF16, MODE>(p, head_dim, align, grid, s)
+              : launch_dt<F16, MODE>(p, head_dim, align, grid, s);
 }
 
 }  // namespace rnq

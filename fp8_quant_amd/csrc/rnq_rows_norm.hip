@@ -3,8 +3,8 @@
 
 namespace rnq {
 
-template hipError_t launch_rows_mode<ROW_Y>(const RowParams&, int, bool, bool, dim3, hipStream_t);
-template hipError_t launch_rows_mode<ROW_Y | ROW_ROPE>(const RowParams&, int, bool, bool, dim3, hipStream_t);
-template hipError_t launch_rows_mode<ROW_Y | ROW_RSTD>(const RowParams&, int, bool, bool, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_Y>(const RowParams&, int, bool, int, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_Y | ROW_ROPE>(const RowParams&, int, bool, int, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_Y | ROW_RSTD>(const RowParams&, int, bool, int, dim3, hipStream_t);
 
 }  // namespace rnq

@@ -3,9 +3,9 @@
 
 namespace rnq {
 
-template hipError_t launch_rows_mode<ROW_QUANT>(const RowParams&, int, bool, bool, dim3, hipStream_t);
-template hipError_t launch_rows_mode<ROW_QUANT | ROW_ROPE>(const RowParams&, int, bool, bool, dim3, hipStream_t);
-template hipError_t launch_rows_mode<ROW_QUANT | ROW_Y>(const RowParams&, int, bool, bool, dim3, hipStream_t);
-template hipError_t launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y>(const RowParams&, int, bool, bool, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_QUANT>(const RowParams&, int, bool, int, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_QUANT | ROW_ROPE>(const RowParams&, int, bool, int, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_QUANT | ROW_Y>(const RowParams&, int, bool, int, dim3, hipStream_t);
+template hipError_t launch_rows_mode<ROW_QUANT | ROW_ROPE | ROW_Y>(const RowParams&, int, bool, int, dim3, hipStream_t);
 
 }  // namespace rnq
