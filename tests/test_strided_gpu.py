@@ -169,6 +169,8 @@ def test_norm_rope_pos_full_size():
     (96, 64, 32, 4, 16, True),      # [T, 4, N] view with padded token stride
     (80, 256, 128, 8, 0, False),    # contiguous x, per-token table
     (40, 512, 256, 2, 24, True),
+    (256, 128, 64, 1, 8, False),    # row-strided x, whole tokens per pass (8 rows of 8 tokens)
+    (96, 64, 32, 4, 16, False),     # [T, 4, N] view with padded stride, 4 tokens per pass
 ])
 def test_rmsnorm_rope_ex_views(M, N, R, rpt, pad, with_pos):
     T = M // rpt
