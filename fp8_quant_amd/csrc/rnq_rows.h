@@ -176,7 +176,11 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr bool POS = (MODE & ROW_POS) != 0;
   constexpr int D = 16 * L;
   constexpr int G = 64 / L;
-  __shared__ float w_lds[2 * D];
+  // each wave stages its own copy of both tensors' weights (fp32): no
+  // workgroup barrier, so a wave starts on its first pass as soon as that
+  // pass's input has arrived (a barrier made every wave wait for the slowest
+  // first input of its workgroup)
+  __shared__ float w_lds[RW * 2 * D];
   // aligned rope passes: each wave stages the pass's cos and sin rows here
   // (several tokens' rows, at most 1 KB of each, when a pass holds whole tokens)
   constexpr bool STAGED = ALIGNED && ROPE;
@@ -187,6 +191,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   const uint32_t lane = tid & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t u = lane % L;
+  float* const w_wave = w_lds + wave * (2 * D);
   const uint32_t slot = lane / L;
 
   // XCD-aware renumbering: hardware places workgroup b on XCD b % 8; give the
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   }
   const uint32_t gw = blk * RW + wave;
   const uint32_t W = p.waves, n = p.per_wave, last = p.passes - 1;
-  // (waves past p.waves, at most RW - 1, load clamped passes and leave after the barrier)
+  // (waves past p.waves, at most RW - 1, leave before their first load)
 #if RNQ_ROWS_CHUNKED
   auto pass_of = [&](uint32_t i) { return min(gw * n + i, last); };
 #else
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
     constexpr bool XCH = decltype(opts)::xch;
     const Loc& r = s.loc;
-    const float* w = w_lds + (r.second ? D : 0);
+    const float* w = w_wave + (r.second ? D : 0);
 
     // ---- sum of squares: fp64 (exact for 16-bit inputs), reduced over the row's lanes
     float xv[16];
@@ -448,36 +453,37 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr int NS = STAGED ? NS_STAGED : 2;  // (two: the register table ring alternates)
   // ---- software pipeline over this wave's n passes: input NS - 1 passes
   // ahead, table values one pass ahead (ring slots are compile-time indices).
-  // The first loads go out before the weights are staged.
   Data d[NS];
   Table tb[2];
+  if (gw >= W) return;
+  // ---- weights of both tensors: 16-byte chunks (D / 8 per tensor), loaded
+  // before any input so that waiting for them never waits for an input; lane
+  // l loads chunk l % (D / 4) (and l + 64 when D = 512) and stores it in the
+  // wave's slot as fp32
+  constexpr uint32_t WCH = D / 4;                     // chunks of both tensors
+  constexpr uint32_t WPL = WCH > 64 ? WCH / 64 : 1;   // chunks per lane
+  uint4 wc[WPL];
+#pragma unroll
+  for (uint32_t i = 0; i < WPL; ++i) {
+    const uint32_t c = (lane + 64 * i) % WCH;
+    const uint16_t* src = (c < D / 8 ? p.w0 : (p.heads0 < p.heads ? p.w1 : p.w0)) + 8 * (c % (D / 8));
+    wc[i] = *(const uint4*)src;
+  }
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) load_data(d[k], pass_of(k));
   if constexpr (STAGED && POS) load_staged_table(d[0]);
   if constexpr (!STAGED) load_table(tb[0], d[0].loc);
-
-  // ---- weights of both tensors, fp32, in LDS (every thread loads a chunk, so
-  // that no global access is conditional; the first D / 8 threads store them)
-  {
-    const uint32_t c = tid % (D / 8);
-    const uint4 w0c = *(const uint4*)(p.w0 + 8 * c);
-    const uint4 w1c = *(const uint4*)((p.heads0 < p.heads ? p.w1 : p.w0) + 8 * c);
-    if (tid < D / 8) {
-      float f[8];
-      unpack8<DT>(w0c, f);
+  // (lanes past the chunks store a copy of the same values: no branch around
+  // the loads' use, which would let the compiler sink them under it)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w_lds[8 * tid + i] = f[i];
-      unpack8<DT>(w1c, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w_lds[D + 8 * tid + i] = f[i];
-    }
+  for (uint32_t i = 0; i < WPL; ++i) {
+    const uint32_t c = (lane + 64 * i) % WCH;
+    float f[8];
+    unpack8<DT>(wc[i], f);
+    float* dst = w_wave + (c < D / 8 ? 0 : D) + 8 * (c % (D / 8));
+    *(float4*)dst = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
   }
-  // everything loaded so far has landed: the loop then starts from the same
-  // outstanding-access count on every entry, which keeps the compiler's
-  // memory-counter waits inside the loop exact
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (gw >= W) return;
 
   // Issue priority by progress (launches whose waves are all resident at once):
   // a SIMD's arbiter favours its oldest wave, so the four waves of a SIMD would
