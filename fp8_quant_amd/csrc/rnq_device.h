@@ -51,6 +51,36 @@ struct F16 {
   }
 };
 
+// fp16 values kept as their bits (low 16 bits of a register) where the only
+// consumers are further products and the store: rounding to fp16 is then one
+// conversion, with no conversion back to fp32.
+// a rounded to fp16 (nearest even), as bits; the empty asm keeps the product
+// that made a from being folded into a mixed-precision fma that rounds once
+__device__ __forceinline__ uint32_t f16_bits(float a) {
+  asm volatile("" : "+v"(a));
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a);
+}
+// RN(h * b) in fp32 for an fp16 value h given as bits: one mixed-precision fma
+// with a -0 addend (x + -0 = x for every x, -0 included, so the result is the
+// fp32 product's rounding and sign; a +0 addend would turn a -0 product into
+// +0). The compiler would rewrite an fma with a -0 addend into a plain
+// multiply, which needs h converted first. The addend is the inline constant 0
+// under the negate modifier: `neg(0)` (a bare `-0` assembles as integer 0).
+__device__ __forceinline__ float mul_f16_f32(uint32_t h, float b) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(b));
+  return r;
+}
+// 8 fp16 values given as bits -> one 16-byte chunk
+__device__ __forceinline__ uint4 pack8_bits(const uint32_t* h) {
+  uint4 v;
+  v.x = (h[0] & 0xffffu) | (h[1] << 16);
+  v.y = (h[2] & 0xffffu) | (h[3] << 16);
+  v.z = (h[4] & 0xffffu) | (h[5] << 16);
+  v.w = (h[6] & 0xffffu) | (h[7] << 16);
+  return v;
+}
+
 // 8 consecutive 16-bit values (one 16-byte chunk) <-> 8 floats
 template <class DT>
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {

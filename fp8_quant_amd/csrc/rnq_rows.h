@@ -319,9 +319,17 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     const float4 wb0 = *(const float4*)(w + off_b), wb1 = *(const float4*)(w + off_b + 4);
     const float wv[16] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w,
                           wb0.x, wb0.y, wb0.z, wb0.w, wb1.x, wb1.y, wb1.z, wb1.w};
+    // (fp16 outputs that are only stored stay as fp16 bits: h)
+    constexpr bool H16 = __is_same(DT, F16) && !QUANT;
     float y[16];
+    uint32_t h[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) y[e] = DT::round((xv[e] * rstd) * wv[e]);
+    for (int e = 0; e < 16; ++e) {
+      if constexpr (H16)
+        h[e] = f16_bits((xv[e] * rstd) * wv[e]);
+      else
+        y[e] = DT::round((xv[e] * rstd) * wv[e]);
+    }
 
     // positions mode: the next pass's table chunks, now that its row number
     // (a scalar load issued with its input) has arrived; still before this
@@ -365,9 +373,15 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
         const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float lo = y[e], hi = y[8 + e];
-          y[e] = DT::round((lo * cc[e]) - (hi * ss[e]));
-          y[8 + e] = DT::round((hi * cc[e]) + (lo * ss[e]));
+          if constexpr (H16) {
+            const uint32_t lo = h[e], hi = h[8 + e];
+            h[e] = f16_bits(mul_f16_f32(lo, cc[e]) - mul_f16_f32(hi, ss[e]));
+            h[8 + e] = f16_bits(mul_f16_f32(hi, cc[e]) + mul_f16_f32(lo, ss[e]));
+          } else {
+            const float lo = y[e], hi = y[8 + e];
+            y[e] = DT::round((lo * cc[e]) - (hi * ss[e]));
+            y[8 + e] = DT::round((hi * cc[e]) + (lo * ss[e]));
+          }
         }
       }
     }
@@ -378,13 +392,15 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
     if constexpr (WY) {
       // the values are already rounded: packing them is exact
       uint16_t* ybase = (r.second ? p.y1 : p.y0) + rbase;
+      const uint4 ya = H16 ? pack8_bits(h) : pack8<DT>(y);
+      const uint4 yb = H16 ? pack8_bits(h + 8) : pack8<DT>(y + 8);
       if constexpr (ALIGNED) {
         const rsrc_t ry = make_rsrc(ybase, 2u * G * D);
-        buf_store16(ry, 2u * ea, pack8<DT>(y));
-        buf_store16(ry, 2u * eb, pack8<DT>(y + 8));
+        buf_store16(ry, 2u * ea, ya);
+        buf_store16(ry, 2u * eb, yb);
       } else {
-        *(uint4*)((char*)ybase + 2u * ea) = pack8<DT>(y);
-        *(uint4*)((char*)ybase + 2u * eb) = pack8<DT>(y + 8);
+        *(uint4*)((char*)ybase + 2u * ea) = ya;
+        *(uint4*)((char*)ybase + 2u * eb) = yb;
       }
     }
     // every lane of the row stores the same value

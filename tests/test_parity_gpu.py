@@ -368,6 +368,72 @@ def test_cross_entry_rope_zero_equals_rmsnorm():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+FP16_SPECIALS = [
+    # N, R, rows_per_token, positions
+    (64, 64, 1, False),
+    (128, 64, 1, False),    # passes of whole tokens
+    (128, 64, 4, False),
+    (128, 128, 8, True),    # position-indexed table rows
+    (256, 128, 2, False),
+    (512, 16, 1, False),
+    (128, 0, 1, False),     # no tail
+]
+
+
+@pytest.mark.parametrize("N,R,rpt,with_pos", FP16_SPECIALS, ids=[f"N{n}R{r}h{h}{'p' if p else ''}"
+                                                                 for n, r, h, p in FP16_SPECIALS])
+def test_rmsnorm_rope_fp16_signed_zeros_and_subnormals(N, R, rpt, with_pos):
+    """fp16 path R bit for bit where the outputs are -0 / +0 (zero rows of either
+    sign, zero weights of either sign, zero and unit table entries), fp16
+    subnormals (tiny weights, a row dominated by one element, tiny table
+    entries) and products that underflow fp32."""
+    T = 48
+    M = T * rpt
+    g = torch.Generator("cpu").manual_seed(N * 7 + R + rpt)
+    x = torch.randn(M, N, generator=g)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, ::2] = -0.0
+    x[2, 1::2] = 0.0
+    x[2, 3] = 1.5
+    x[3] = 1e-3 * torch.randn(N, generator=g)
+    x[3, 5] = 60000.0
+    x[4, : N // 2] = -0.0
+    w = 1 + 0.1 * torch.randn(N, generator=g)
+    w[::5] *= -1
+    w[1::7] = 0.0
+    w[2::7] = -0.0
+    w[3::11] = 1e-5
+    w[4::13] = -3e-7
+    x, w = x.to(torch.float16), w.to(torch.float16)
+    rows = 2 * T if with_pos else T
+    cos, sin = workloads.rope_table(np.arange(rows) * 5, R, 10000.0)
+    cos, sin = cos.copy(), sin.copy()
+    if R:
+        cos[::3, ::4] = 0.0
+        sin[::3, ::4] = 1.0
+        cos[1::3, 1::4] = -0.0
+        sin[1::3, 1::4] = -1.0
+        cos[2::3, 2::4] = 1e-30
+        sin[2::3, 3::4] = -1e-38
+    pos = torch.randint(0, rows, (T,), generator=g, dtype=torch.int32) if with_pos else None
+    print(f"[fp16 specials] N{N} R{R} rows_per_token {rpt} positions {with_pos}", flush=True)
+    y = rnq.rmsnorm_rope(gpu(x), gpu(w), gpu(torch.from_numpy(cos)) if R else None,
+                         gpu(torch.from_numpy(sin)) if R else None, rows_per_token=rpt,
+                         positions=None if pos is None else gpu(pos))
+    torch.cuda.synchronize()
+    t = np.arange(T) if pos is None else pos.numpy().astype(np.int64)
+    ref = oracle.rmsnorm_rope(workloads.bits(x), workloads.bits(w), cos[t], sin[t], 1e-6, "fp16", rpt)
+    got = workloads.bits(y)
+    assert (got == 0x8000).any() and (got == 0).any()  # both zeros occur
+    assert_rows_match(f"fp16 specials N{N} R{R}", got, None, None, ref, None, None,
+                      unproven_rows(workloads.bits(x), "fp16"))
+    if R == 0:
+        y0 = rnq.rmsnorm(gpu(x), gpu(w))
+        torch.cuda.synchronize()
+        assert np.array_equal(workloads.bits(y0), got)
+
+
 def test_invalid_arguments_raise_before_launch():
     x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
     w = torch.zeros(128, dtype=torch.bfloat16, device="cuda")
