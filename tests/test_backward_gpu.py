@@ -185,12 +185,12 @@ def test_autograd_only_weight_grad():
 
 EDGE = [
     # M, N, R, dtype, rows_per_token
-    (4096, 4096, 0, torch.bfloat16, 1),     # wide rows: 512 blocks of 8 rows
-    (4100, 2048, 0, torch.bfloat16, 1),     # ragged: 456 blocks of 9 rows, the last one of 5
-    (16384, 128, 0, torch.float16, 1),      # narrow rows: 512 blocks of 32
+    (4096, 4096, 0, torch.bfloat16, 1),     # wide rows: 256 blocks of 16 rows
+    (4100, 2048, 0, torch.bfloat16, 1),     # ragged: 242 blocks of 17 rows, the last one of 3
+    (16384, 128, 0, torch.float16, 1),      # narrow rows: 256 blocks of 64
     (16384, 128, 64, torch.float16, 1),     # narrow rows through the RoPE backward
     (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward
-    (20000, 256, 0, torch.bfloat16, 1),     # above 8192 rows: 256 blocks
+    (20000, 256, 0, torch.bfloat16, 1),     # 254 blocks of 79, the last one of 13
 ]
 
 
