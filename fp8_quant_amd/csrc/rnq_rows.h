@@ -196,14 +196,20 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 
   // XCD-aware renumbering: hardware places workgroup b on XCD b % 8; give the
   // workgroups of one XCD a contiguous stretch of the wave numbers.
+  // (a select, not a branch: the compiler issues no kernel-argument load past
+  // a branch, so a branch here made the argument loads two dependent rounds,
+  // each a full memory latency before the first input load goes out)
   uint32_t blk = blockIdx.x;
   {
     const uint32_t nb = gridDim.x, full = nb & ~7u;
-    if (blk < full) blk = (blk & 7u) * (full >> 3) + (blk >> 3);
+    const uint32_t moved = (blk & 7u) * (full >> 3) + (blk >> 3);
+    blk = blk < full ? moved : blk;
   }
   const uint32_t gw = blk * RW + wave;
   const uint32_t W = p.waves, n = p.per_wave, last = p.passes - 1;
-  // (waves past p.waves, at most RW - 1, leave before their first load)
+  // (waves past p.waves, at most RW - 1 in the last workgroup, repeat passes of
+  // other waves, clamped into range, and write identical bytes: an early exit
+  // would be a branch ahead of the kernel-argument loads, see below)
 #if RNQ_ROWS_CHUNKED
   auto pass_of = [&](uint32_t i) { return min(gw * n + i, last); };
 #else
@@ -214,17 +220,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   const uint32_t R = ROPE ? p.rope : 0u, half = R / 2;
   const uint32_t n_plain = (D - R) / 16;  // units outside the rope tail
   const bool rope_lane = u >= n_plain;
-  uint32_t off_a, off_b, cs_off;
-  if (!rope_lane) {
-    off_a = 16 * u;
-    off_b = off_a + 8;
-    cs_off = 0;
-  } else {
-    const uint32_t j = u - n_plain;
-    off_a = (D - R) + 8 * j;
-    off_b = off_a + half;
-    cs_off = 8 * j;
-  }
+  // (selects, not an if / else: no branch ahead of the kernel-argument loads,
+  // see the renumbering below)
+  const uint32_t j_tail = u - n_plain;  // (used on rope lanes only)
+  const uint32_t off_a = rope_lane ? (D - R) + 8 * j_tail : 16 * u;
+  const uint32_t off_b = rope_lane ? off_a + half : off_a + 8;
+  const uint32_t cs_off = rope_lane ? 8 * j_tail : 0u;
   // aligned passes: element offsets of this lane's chunks from the pass's first row
   // (outputs: contiguous rows; inputs: tokens xs0 elements apart when a pass holds
   // several tokens, the row's place inside its token otherwise)
@@ -471,7 +472,6 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   // ahead, table values one pass ahead (ring slots are compile-time indices).
   Data d[NS];
   Table tb[2];
-  if (gw >= W) return;
   // ---- weights of both tensors: 16-byte chunks (D / 8 per tensor), loaded
   // before any input so that waiting for them never waits for an input; lane
   // l loads chunk l % (D / 4) (and l + 64 when D = 512) and stores it in the
