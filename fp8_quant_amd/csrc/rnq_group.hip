@@ -30,7 +30,13 @@ constexpr int GT = 256;       // threads per workgroup
 constexpr int GWV = GT / 64;  // waves
 constexpr uint32_t kMaxRope = 1024;
 
-template <class DT, int KC, int GL, bool QUANT = true>
+// (Every kernel argument a workgroup needs before its first input load is
+// read in one round: no branch precedes those loads, since the compiler issues
+// no argument load past one. The token comes from a host-computed
+// multiply-shift, the launcher gives every call a token stride and the table's
+// row count, and a position-indexed table is a template case; with positions
+// the table row is a second, dependent round, after the input loads.)
+template <class DT, int KC, int GL, bool QUANT = true, bool POS = false>
 __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   constexpr uint32_t kOutOfRange = 0x80000000u;
   __shared__ double part[GWV];
@@ -50,16 +56,9 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     ok[k] = ch[k] < nch;
     off[k] = ok[k] ? 16u * ch[k] : kOutOfRange;
   }
-  // the row's token, its place in a (possibly strided) view, and its table row
-  const uint32_t tok = row / p.rows_per_token;
-  const size_t xoff = p.xs == 0 ? (size_t)row * p.N : (size_t)tok * p.xs + (size_t)(row - tok * p.rows_per_token) * p.N;
-  uint32_t trow = tok;
-  if (p.positions != nullptr) {
-    // a workgroup-uniform index read through the constant address space (a
-    // scalar load; the kernel never writes positions)
-    typedef const __attribute__((address_space(4))) int32_t const_i32;
-    trow = min((uint32_t)((const_i32*)p.positions)[tok], p.max_pos - 1);
-  }
+  // the row's token and its place in a (possibly strided) view
+  const uint32_t tok = (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);
+  const size_t xoff = (size_t)tok * p.xs + (size_t)(row - tok * p.rows_per_token) * p.N;
   const rsrc_t rx = make_rsrc(p.x + xoff, row_bytes);
   const rsrc_t rw = make_rsrc(p.w, row_bytes);
   uint4 xr[KC], wr[KC];
@@ -67,6 +66,14 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   for (int k = 0; k < KC; ++k) {
     xr[k] = buf_load16_nt(rx, off[k]);
     wr[k] = buf_load16(rw, off[k]);
+  }
+  // the token's table row
+  uint32_t trow = tok;
+  if constexpr (POS) {
+    // a workgroup-uniform index read through the constant address space (a
+    // scalar load; the kernel never writes positions)
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    trow = min((uint32_t)((const_i32*)p.positions)[tok], p.max_pos - 1);
   }
   // the rope tail's cos/sin values go out with the row: a thread's chunks are
   // 256 apart and the tail is at most 128 chunks, so a thread owns at most one
@@ -80,8 +87,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
       const uint32_t j = ch[k] - t0;
       toff = 4u * (trow * half + 8u * (j < hc ? j : j - hc));
     }
-  const uint32_t table_rows = p.positions != nullptr ? p.max_pos : (p.M - 1) / p.rows_per_token + 1;
-  const uint32_t table_bytes = R > 0 ? table_rows * half * 4u : 0u;
+  const uint32_t table_bytes = R > 0 ? p.max_pos * half * 4u : 0u;
   const rsrc_t rcos = make_rsrc(p.cos, table_bytes), rsin = make_rsrc(p.sin, table_bytes);
   const float4 tc0 = buf_load16f(rcos, toff), tc1 = buf_load16f(rcos, toff + 16u);
   const float4 ts0 = buf_load16f(rsin, toff), ts1 = buf_load16f(rsin, toff + 16u);
@@ -241,33 +247,45 @@ static hipError_t launch_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <class DT>
+template <class DT, bool POS>
 static hipError_t launch_norm_rope_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
   const uint32_t nch = p.N / 8;
   if (nch <= GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 1, 0, false>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 1, 0, false, POS>), g, dim3(GT), 0, s, p);
   else if (nch <= 2 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 2, 0, false>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 2, 0, false, POS>), g, dim3(GT), 0, s, p);
   else if (nch <= 4 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 4, 0, false>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 4, 0, false, POS>), g, dim3(GT), 0, s, p);
   else if (nch <= 8 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 8, 0, false>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 8, 0, false, POS>), g, dim3(GT), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// the row -> token division, a token stride for every call, and the table's
+// row count (position-indexed: the caller's; otherwise one row per token)
+static void set_rows(GroupQuantParams& p) {
+  div_magic_for(p.rows_per_token, p.div_magic, p.div_shift);
+  if (p.xs == 0) p.xs = (uint64_t)p.rows_per_token * p.N;
+  if (p.positions == nullptr) p.max_pos = (p.M - 1) / p.rows_per_token + 1;
 }
 
 hipError_t launch_wide_norm_rope(GroupQuantParams p, bool bf16, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   if (p.rope > kMaxRope || p.y == nullptr || p.rows_per_token == 0) return hipErrorInvalidValue;
   p.group_size = 0;
+  set_rows(p);
   const dim3 grid(p.M);
-  return bf16 ? launch_norm_rope_dt<BF16>(p, grid, stream) : launch_norm_rope_dt<F16>(p, grid, stream);
+  if (p.positions != nullptr)
+    return bf16 ? launch_norm_rope_dt<BF16, true>(p, grid, stream) : launch_norm_rope_dt<F16, true>(p, grid, stream);
+  return bf16 ? launch_norm_rope_dt<BF16, false>(p, grid, stream) : launch_norm_rope_dt<F16, false>(p, grid, stream);
 }
 
 hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (p.rope > kMaxRope) return hipErrorInvalidValue;
+  if (p.rope > kMaxRope || p.rows_per_token == 0 || p.positions != nullptr) return hipErrorInvalidValue;
+  set_rows(p);
   p.rcp_fp8_max = 1.0f / p.fp8_max;
   p.scale_floor = 1e-4f / p.fp8_max;
   p.scale_by_rcp = p.fp8_max >= 1.0f ? 1u : 0u;

@@ -109,8 +109,8 @@ struct GroupQuantParams {
   uint8_t* codes;    // [M, N] (quantising mode)
   float* scales;     // [M, N / group_size] (quantising mode)
   const int32_t* positions;  // optional [M / rows_per_token]: table row of each token (clamped into range)
-  uint64_t xs;       // token stride of x in elements (0: contiguous rows)
-  uint32_t max_pos;  // table rows when positions are given
+  uint64_t xs;       // token stride of x in elements (0: contiguous rows; the launcher sets rows_per_token * N)
+  uint32_t max_pos;  // table rows when positions are given (the launcher sets the table's rows otherwise)
   uint32_t M;
   uint32_t N;
   uint32_t rope;
@@ -123,6 +123,7 @@ struct GroupQuantParams {
   float scale_floor;
   uint32_t scale_by_rcp;
   uint32_t clamp;
+  uint32_t div_magic, div_shift;  // row / rows_per_token = (row * div_magic) >> div_shift
 };
 
 hipError_t launch_group_quant(GroupQuantParams p, bool bf16, hipStream_t stream);

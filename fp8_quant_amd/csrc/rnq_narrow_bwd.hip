@@ -46,8 +46,11 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
   const uint32_t ch = lane % L;                    // chunk within the row
   const uint32_t lrow = (tid >> 6) * G + lane / L;  // row within a step
   const uint32_t r0 = blockIdx.x * p.rows_per_block;
-  if (r0 >= p.M) return;  // (not reached with bwd_blocks' partition)
-  const uint32_t nrows = min(p.rows_per_block, p.M - r0);
+  // (bwd_blocks' partition gives every block rows; a block without rows would
+  // read nothing and write a zero partial row. No early exit: a branch here
+  // would come before the kernel-argument loads, and the compiler issues none
+  // past a branch.)
+  const uint32_t nrows = r0 < p.M ? min(p.rows_per_block, p.M - r0) : 0u;
   const uint32_t steps = (nrows + RPI - 1) / RPI;
   const uint32_t span = nrows * row_bytes;  // < 2^31 (checked by the caller)
   const rsrc_t rx = make_rsrc(p.x + (size_t)r0 * D, span);

@@ -131,21 +131,27 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   const uint32_t wave = tid >> 6;
   const uint32_t nch = p.N / 8;
   const uint32_t r0 = blockIdx.x * p.rows_per_block;
-  const uint32_t r1 = min(r0 + p.rows_per_block, p.M);  // r0 < r1: the partition gives every block rows
+  // the partition gives every block rows (r0 < r1); a block without rows would
+  // run no batch and write a zero partial row. (No early exit: a branch here
+  // would come before the kernel-argument loads the first batch needs, and
+  // the compiler issues none past a branch.)
+  const uint32_t r1 = min(r0 + p.rows_per_block, p.M);
+  const uint32_t nrows = r1 > r0 ? r1 - r0 : 0u;
   const uint32_t row_bytes = 2u * p.N;
-  if (r0 >= r1) return;  // (not reached with bwd_partition's blocks)
 
-  extern __shared__ uint4 w_s[];  // the weight row (16-bit values, N * 2 bytes), read where it is used
+  // the weight row (16-bit values, N * 2 bytes, and one spare 16-byte slot),
+  // read where it is used
+  extern __shared__ uint4 w_s[];
   float dw[KC][8];
   bool ok[KC];
   uint32_t off[KC];  // byte offset of the lane's chunk k in a row (out of range past the end)
+  uint4 wcs[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     const uint32_t c = tid + BT * k;
     ok[k] = c < nch;
     off[k] = ok[k] ? 16u * c : kOutOfRange;
-    const uint4 wc = buf_load16(make_rsrc(p.w, row_bytes), off[k]);
-    if (ok[k]) w_s[c] = wc;
+    wcs[k] = buf_load16(make_rsrc(p.w, row_bytes), off[k]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dw[k][i] = 0.f;
   }
@@ -153,7 +159,6 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
     const uint4 wc = w_s[ok[k] ? tid + BT * k : 0u];
     unpack8<DT>(ok[k] ? wc : make_uint4(0, 0, 0, 0), wf);
   };
-  lds_barrier();
 
   // RoPE geometry: R = p.rope columns at the end of the row, chunks t0 .. nch - 1,
   // hc chunks per half; thread-owned table values e = tid + BT m (cos for e < R/2,
@@ -198,6 +203,13 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   uint4 xr[2][RB][KC], gr[2][RB][KC];
   float tr[2][RB][TPT];
   load_batch(r0, xr[0], gr[0], tr[0]);
+  // the weights go to LDS once the first batch is in flight too (they were
+  // loaded first, so waiting for them waits for no row); lanes past the row
+  // store their zeros in the spare slot: a store under a branch would let the
+  // compiler sink the weight load under it, behind the barrier
+#pragma unroll
+  for (int k = 0; k < KC; ++k) w_s[ok[k] ? tid + BT * k : nch] = wcs[k];
+  lds_barrier();
   uint32_t parity = 0;
 
   // one batch; cur / nxt are compile-time ring slots
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(BT) void wide_bwd_kernel(WideBwdParams p) {
   };
 
   // batches alternate between the two ring slots
-  const uint32_t nb = (r1 - r0 + RB - 1) / RB;
+  const uint32_t nb = (nrows + RB - 1) / RB;
   uint32_t b = 0;
   for (; b + 2 <= nb; b += 2) {
     batch(r0 + b * RB, xr[0], gr[0], tr[0], xr[1], gr[1], tr[1]);
@@ -369,7 +381,10 @@ __global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __rest
   const bool ok = 4 * c4 < N;
   const rsrc_t rp = make_rsrc(partial, 4u * blocks * N);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (uint32_t b0 = 0; b0 < blocks; b0 += 64 * RU) {
+  // (blocks >= 1, so the first strip of rows is read without a loop test: no
+  // branch before the kernel-argument loads it needs)
+  uint32_t b0 = 0;
+  do {
     float4 v[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
@@ -380,7 +395,8 @@ __global__ __launch_bounds__(64 * RDW) void dw_reduce_kernel(const float* __rest
     for (int u = 0; u < RU; ++u) {
       acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
     }
-  }
+    b0 += 64 * RU;
+  } while (b0 < blocks);
 #pragma unroll
   for (int m = RCQ; m < 64; m *= 2) {
     acc.x += __shfl_xor(acc.x, m, 64);
@@ -429,7 +445,7 @@ static hipError_t fwd_kc(const WideFwdParams& p, int kc, hipStream_t s) {
 template <class DT, bool SAVED, bool ROPE>
 static hipError_t bwd_kc(const WideBwdParams& p, int kc, dim3 g, hipStream_t s) {
   constexpr int B = RNQ_BWD_BATCH;
-  const size_t lds = 2 * (size_t)p.N;  // the weight row
+  const size_t lds = 2 * (size_t)p.N + 16;  // the weight row and a spare 16-byte slot
   if (p.N <= 2048) {
     hipLaunchKernelGGL((wide_bwd_kernel<DT, 1, 256, B, SAVED, ROPE>), g, dim3(256), lds, s, p);
     return hipGetLastError();
