@@ -89,7 +89,7 @@ EXPORTED_SYMBOLS = (
 
 RNQ_BF16 = 0
 RNQ_F16 = 1
-RNQ_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # the library's static backward scratch (include/rnq.h)
+RNQ_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's static backward scratch (include/rnq.h)
 
 
 class RnqError(RuntimeError):

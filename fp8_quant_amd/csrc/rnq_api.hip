@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -369,7 +370,8 @@ rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const floa
 
 size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
-  return (size_t)bwd_blocks(M, N) * (size_t)N * sizeof(float);
+  const uint32_t blocks = std::max(bwd_blocks(M, N, false), bwd_blocks(M, N, true));
+  return (size_t)blocks * (size_t)N * sizeof(float);
 }
 
 }  // extern "C"
@@ -456,7 +458,7 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
   if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
-  const uint32_t blocks = bwd_blocks(M, N);
+  const uint32_t blocks = bwd_blocks(M, N, rope_dim > 0);
   const uint32_t rows_per_block = (uint32_t)((M + blocks - 1) / blocks);
   // the kernels address the tables (and the narrow one a block's rows) with 32-bit offsets
   const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;

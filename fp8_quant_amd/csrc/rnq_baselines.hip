@@ -305,10 +305,14 @@ hipError_t launch_design(const RowParams& rp, uint32_t rows_per_block, int D, bo
 // writes the 1 KB block w of dst (their XOR), with nontemporal buffer accesses
 // and nothing else.
 __global__ __launch_bounds__(256) void stream_kernel(const uint8_t* src, uint8_t* dst, uint32_t blocks) {
-  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6), lane = threadIdx.x & 63u;
-  if (w >= blocks) return;  // (whole waves)
-  const rsrc_t rs = make_rsrc(src + (size_t)w * 2048u, 2048u);
-  const rsrc_t rd = make_rsrc(dst + (size_t)w * 1024u, 1024u);
+  const uint32_t w = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63u;
+  // waves past the last block read and write nothing (empty descriptors): an
+  // early exit would be a branch ahead of the argument loads, which the
+  // compiler then issues in a second dependent round
+  const bool live = w < blocks;
+  const size_t wb = live ? w : 0u;
+  const rsrc_t rs = make_rsrc(src + wb * 2048u, live ? 2048u : 0u);
+  const rsrc_t rd = make_rsrc(dst + wb * 1024u, live ? 1024u : 0u);
   const uint4 a = buf_load16_nt(rs, 16u * lane);
   const uint4 b = buf_load16_nt(rs, 1024u + 16u * lane);
   buf_store16_nt(rd, 16u * lane, make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w));

@@ -172,8 +172,9 @@ hipError_t launch_design(const RowParams& p, uint32_t rows_per_block, int D, boo
 // src_bytes / 2048 blocks of the memory-floor kernel (0: one empty workgroup)
 hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s);
 
-// Deterministic row partition used by the backward (and its workspace size).
-uint32_t bwd_blocks(int64_t M, int64_t N);
+// Deterministic row partition used by the backward (rope: the RoPE backward);
+// the workspace size covers the larger of the two.
+uint32_t bwd_blocks(int64_t M, int64_t N, bool rope);
 hipError_t launch_wide_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
 // grad_w[j] = sum over b of partial[b, j] in a fixed order
 hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream);

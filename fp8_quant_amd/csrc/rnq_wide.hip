@@ -483,12 +483,15 @@ hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream
 }
 
 // Blocks of contiguous rows, every block owning at least one row: about 256
-// (one workgroup per CU). At 4096 x 4096, 512 blocks (twice the partial rows
-// of grad_w to write and read back) took 25.9 us against 24.9 us.
-uint32_t bwd_blocks(int64_t M, int64_t N) {
+// (one workgroup per CU), or 512 (two) for the RoPE backward up to 8192 rows.
+// At 4096 x 4096: the plain backward 24.8 us with 256 blocks against 26.0 with
+// 512 (half the partial rows of grad_w to write and read back), the RoPE
+// backward 27.9 us with 512 against 30.5 with 256 (its per-batch LDS exchange
+// of the tail needs the second workgroup's waves to hide behind).
+uint32_t bwd_blocks(int64_t M, int64_t N, bool rope) {
   (void)N;
   if (M <= 0) return 1;
-  const int64_t target = 256;
+  const int64_t target = rope && M <= 8192 ? 512 : 256;
   const int64_t rpb = (M + target - 1) / target;
   return (uint32_t)((M + rpb - 1) / rpb);
 }

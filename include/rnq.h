@@ -166,9 +166,9 @@ rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y
                                 void* stream);
 
 /* Size of the library's static device scratch used by rnq_rmsnorm_rope_bwd_noalloc:
- * 16 MiB, enough for the grad_w partials of every shape the backward accepts
+ * 32 MiB, enough for the grad_w partials of every shape the backward accepts
  * (at most 512 partial rows of N <= 16384 fp32 values). */
-#define RNQ_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+#define RNQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
 
 /*
  * rnq_rmsnorm_rope_bwd without a caller workspace, for callers that cannot

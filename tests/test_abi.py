@@ -125,10 +125,9 @@ def test_rmsnorm_argument_validation():
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 2048, 1, 1e-6, 0, None) == 3  # tail > 1024
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 1  # wide rows, no table
     need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 4096)
-    assert need == 256 * 4096 * 4  # 256 blocks of 16 rows
+    assert need == 512 * 4096 * 4  # the RoPE backward's 512 blocks of 8 rows (the plain one takes 256 of 16)
     assert lib.rnq_rmsnorm_bwd_workspace_size(16384, 4096) == 256 * 4096 * 4
-    assert lib.rnq_rmsnorm_bwd_workspace_size(257, 1024) == 129 * 1024 * 4  # two rows per block, the last one of 1
-    assert lib.rnq_rmsnorm_bwd_workspace_size(200, 1024) == 200 * 1024 * 4  # one row per block
+    assert lib.rnq_rmsnorm_bwd_workspace_size(257, 1024) == 257 * 1024 * 4  # one row per block (RoPE partition)
     assert lib.rnq_rmsnorm_bwd_workspace_size(0, 4096) == 0
     assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, 4096, 4096, 1e-6, 0, None) == 5
     assert lib.rnq_rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, need, 4096, 4096, 1e-6, 0, None) == 5
@@ -229,7 +228,7 @@ def test_noalloc_bwd_argument_validation():
     # every shape the backward accepts fits the static scratch
     assert lib.rnq_rmsnorm_bwd_workspace_size(8192, 16384) == rnq.RNQ_NOALLOC_SCRATCH_BYTES
     assert lib.rnq_rmsnorm_bwd_workspace_size((1 << 31) - 1, 16384) <= rnq.RNQ_NOALLOC_SCRATCH_BYTES
-    assert "RNQ_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)" in open(os.path.join(ROOT, "include", "rnq.h")).read()
+    assert "RNQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)" in open(os.path.join(ROOT, "include", "rnq.h")).read()
 
 
 def test_autograd_refuses_cpu_tensors():

@@ -188,8 +188,8 @@ EDGE = [
     (4096, 4096, 0, torch.bfloat16, 1),     # wide rows: 256 blocks of 16 rows
     (4100, 2048, 0, torch.bfloat16, 1),     # ragged: 242 blocks of 17 rows, the last one of 3
     (16384, 128, 0, torch.float16, 1),      # narrow rows: 256 blocks of 64
-    (16384, 128, 64, torch.float16, 1),     # narrow rows through the RoPE backward
-    (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward
+    (16384, 128, 64, torch.float16, 1),     # narrow rows through the RoPE backward: 256 blocks of 64
+    (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward: 512 blocks of 4
     (20000, 256, 0, torch.bfloat16, 1),     # 254 blocks of 79, the last one of 13
 ]
 
@@ -202,8 +202,10 @@ def test_grad_w_counts_block_edge_rows_once(M, N, R, dtype, rpt):
     reduction moves a column of grad_w by a whole row's gy * xn, which the
     per-column bound 1e-4 * sum over rows of |gy * xn| catches (the 2e-2 rule
     of the full-size tests cannot see one row out of thousands)."""
-    blocks = rnq.rnq_rmsnorm_bwd_workspace_size(M, N) // (4 * N)
-    rpb = -(-M // blocks)
+    # the partition: about 256 blocks, or 512 for the RoPE backward up to 8192 rows
+    target = 512 if (R and M <= 8192) else 256
+    rpb = -(-M // target)
+    blocks = -(-M // rpb)
     picks = sorted({r for b in (0, blocks // 2, blocks - 1) for r in (b * rpb, min(b * rpb + rpb, M) - 1)} | {M - 1})
     print(f"[bwd] grad_w edge rows M{M} N{N} R{R}: {blocks} blocks of {rpb}, rows {picks}", flush=True)
     x, w, gy, cos, sin = _case(M, N, R, seed=M + N + R, dtype=dtype, rows_per_token=rpt)

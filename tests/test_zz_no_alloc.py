@@ -69,7 +69,8 @@ CASES = [
     # (first call), (second, smaller call)
     ("wide rows", (4096, 4096, 0, torch.bfloat16, 1, False), (1000, 2048, 0, torch.bfloat16, 1, False)),
     ("rope tail", (16384, 128, 64, torch.float16, 1, False), (520, 128, 64, torch.float16, 4, True)),
-    ("full scratch", (8192, 16384, 0, torch.bfloat16, 1, True), (3, 64, 0, torch.bfloat16, 1, False)),
+    # the RoPE backward's 512 blocks x 16384 fp32 partials: every byte of the static scratch
+    ("full scratch", (8192, 16384, 128, torch.bfloat16, 1, True), (3, 64, 0, torch.bfloat16, 1, False)),
 ]
 
 
