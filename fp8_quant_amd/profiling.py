@@ -15,7 +15,7 @@ Usage::
 
     python -m fp8_quant_amd.profiling stats TRACE_CSV OUT_MD --command "..."
     python -m fp8_quant_amd.profiling counters FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV \
-        COPY_BYTES OUT_MD --command "..."
+        COPY_BYTES OUT_MD --command "..." [--sq SQ_CSV]
     python -m fp8_quant_amd.profiling traffic FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV \
         COPY_BYTES OUT_JSON --kernel rows_kernel --grid 1310720 --command "..."
 """
@@ -136,30 +136,51 @@ def _per_kernel(counter_csv: str, counter: str) -> dict:
     return {k: statistics.median(v.values()) for k, v in per.items()}
 
 
-def write_counters_md(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out_md, command) -> None:
+SQ_COLUMNS = ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES")
+
+
+def write_counters_md(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out_md, command,
+                      sq_csv=None, skip=("copyBuffer", "FillFunctor")) -> None:
+    """Calibrated HBM bytes per dispatch of every (kernel, grid); with ``sq_csv``
+    (an SQ counter pass of the same command) also the waves and the instruction
+    mix per wave."""
     cf = counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copy", None)
     cw = counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copy", None)
     f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
     fetch, write = _per_kernel(fetch_csv, "FETCH_SIZE"), _per_kernel(write_csv, "WRITE_SIZE")
+    sq = {c: _per_kernel(sq_csv, c) for c in ("SQ_WAVES",) + SQ_COLUMNS} if sq_csv else None
     lines = [
-        "# HBM bytes per dispatch by kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)",
+        "# HBM bytes per dispatch by kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)"
+        + (" and instruction mix per wave" if sq else ""),
         "",
-        f"Command: `{command}` (one pass per counter), and `python3 bench.py --calibrate-copy` under the same",
-        f"counters for the calibration: a {copy_bytes}-byte copy reads {cf:.0f} KiB and writes {cw:.0f} KiB as",
-        f"counted, so FETCH is scaled by {f_scale:.4f} and WRITE by {w_scale:.4f}.",
+        f"Command: `{command}` (one pass per counter group), and `python3 bench.py --calibrate-copy` under",
+        f"FETCH_SIZE and WRITE_SIZE for the calibration: a {copy_bytes}-byte copy reads {cf:.0f} KiB and writes",
+        f"{cw:.0f} KiB as counted, so FETCH is scaled by {f_scale:.4f} and WRITE by {w_scale:.4f}. Medians over",
+        "the profiled dispatches of each (kernel, grid).",
         "",
-        "| kernel | grid (threads) | workgroup | read MB | written MB | total MB |",
-        "|---|---|---|---|---|---|",
     ]
+    head = "| kernel | grid (threads) | workgroup | read MB | written MB | total MB |"
+    rule = "|---|---|---|---|---|---|"
+    if sq:
+        head += " waves | " + " | ".join(c[3:].replace("INSTS_", "").lower() + " / wave" for c in SQ_COLUMNS) + " |"
+        rule += "---|" * (1 + len(SQ_COLUMNS))
+    lines += [head, rule]
     for key in sorted(fetch, key=lambda k: -fetch[k]):
-        if "copyBuffer" in key[0] or key not in write:
+        if any(t in key[0] for t in skip) or key not in write:
             continue
         rd = fetch[key] * 1024.0 * f_scale / 1e6
         wr = write[key] * 1024.0 * w_scale / 1e6
         name = key[0].replace("|", "\\|")
         if len(name) > 80:
             name = name[:77] + "..."
-        lines.append(f"| `{name}` | {key[1]} | {key[2]} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} |")
+        row = f"| `{name}` | {key[1]} | {key[2]} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} |"
+        if sq:
+            waves = sq["SQ_WAVES"].get(key)
+            if waves:
+                row += f" {waves:.0f} | " + " | ".join(f"{sq[c].get(key, float('nan')) / waves:.1f}" for c in SQ_COLUMNS) + " |"
+            else:
+                row += " |" * (1 + len(SQ_COLUMNS))
+        lines.append(row)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -216,6 +237,7 @@ def main(argv=None) -> int:
     c.add_argument("copy_bytes", type=int)
     c.add_argument("out_md")
     c.add_argument("--command", required=True)
+    c.add_argument("--sq", default=None, help="an SQ counter pass of the same command (instruction mix per wave)")
     b = sub.add_parser("traffic")
     for n in ("fetch_csv", "write_csv", "copy_fetch_csv", "copy_write_csv"):
         b.add_argument(n)
@@ -231,7 +253,7 @@ def main(argv=None) -> int:
         write_stats_md(args.trace_csv, args.out_md, args.command, headline=hl)
     elif args.cmd == "counters":
         write_counters_md(args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv, args.copy_bytes,
-                          args.out_md, args.command)
+                          args.out_md, args.command, sq_csv=args.sq)
     else:
         rec = write_traffic_json(args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv,
                                  args.copy_bytes, args.out_json, args.kernel, args.grid, args.command,
