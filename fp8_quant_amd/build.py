@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-ffp-contract=off",  # every multiply and add rounds on its own (no implicit FMA)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 14 dwords of kernel arguments arrive in scalar registers at wave
+    # launch (gfx950 preloading): kernels whose leading arguments are scalars
+    # issue their first loads without a load of the kernel arguments
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-function",
 ]

@@ -102,52 +102,71 @@ struct Table {
   float4 c0, c1, s0, s1;  // this lane's values (per-lane rows)
 };
 
-__device__ __forceinline__ uint32_t div_heads(const RowParams& p, uint32_t row) {
-  return (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);  // row / heads, exact below 2^31
+// The fields a wave needs before its first input load. They reach the kernel
+// as leading scalar arguments (14 dwords), which gfx950 preloads into scalar
+// registers at wave launch: the first input loads then go out without
+// waiting for a load of the kernel arguments (one memory latency per launch).
+// On passes of whole tokens (one tensor, no x1) the x1 slot carries the token
+// shift and the pass's input span instead.
+struct RowHot {
+  const uint16_t* x0;
+  uint64_t x1_or_mt;  // x1, or tok_shift | xspan << 32
+  uint64_t xs0, xs1;
+  uint32_t waves, passes, heads, heads0, div_magic;
+  uint32_t shift_rope;  // div_shift | rope << 8
+  __device__ __forceinline__ uint32_t div_shift() const { return shift_rope & 0xffu; }
+  __device__ __forceinline__ uint32_t rope() const { return shift_rope >> 8; }
+  __device__ __forceinline__ const uint16_t* x1() const { return (const uint16_t*)x1_or_mt; }
+  __device__ __forceinline__ uint32_t tok_shift() const { return (uint32_t)x1_or_mt; }
+  __device__ __forceinline__ uint32_t xspan() const { return (uint32_t)(x1_or_mt >> 32); }
+};
+
+__device__ __forceinline__ uint32_t div_heads(const RowHot& h, uint32_t row) {
+  return (uint32_t)(((uint64_t)row * h.div_magic) >> h.div_shift());  // row / heads, exact below 2^31
 }
 
 template <int G, int D, bool ALIGNED, bool POS, bool MT>
-__device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_t slot) {
+__device__ __forceinline__ Loc locate(const RowParams& p, const RowHot& hp, uint32_t pass, uint32_t slot) {
   Loc r;
   if constexpr (MT) {
     // whole tokens of tensor 0: the pass's first row and token are wave-uniform
     static_assert(ALIGNED && !POS, "several tokens per pass: aligned, table rows read in order");
     const uint32_t row0 = __builtin_amdgcn_readfirstlane(pass * (uint32_t)G);
-    const uint32_t t = __builtin_amdgcn_readfirstlane(row0 >> p.tok_shift);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(row0 >> hp.tok_shift());
     r.second = false;
     r.tok = t;
     r.ri0 = row0;
     r.ri = row0 + slot;
     r.row = row0 + slot;
-    r.xoff = (uint64_t)t * p.xs0;
+    r.xoff = (uint64_t)t * hp.xs0;
   } else if constexpr (ALIGNED) {
     // the whole pass lies inside one token and one tensor, and the launch
     // holds whole passes only: everything but the slot is wave-uniform
     // (readfirstlane: keep the wave-uniform values in scalar registers through
     // every control-flow merge, so descriptors built from them stay scalar)
     const uint32_t row0 = __builtin_amdgcn_readfirstlane(pass * (uint32_t)G);
-    const uint32_t t = __builtin_amdgcn_readfirstlane(div_heads(p, row0));
-    const uint32_t h0 = row0 - t * p.heads;
-    r.second = h0 >= p.heads0;
-    const uint32_t hk = __builtin_amdgcn_readfirstlane(r.second ? h0 - p.heads0 : h0);  // head inside its tensor
-    const uint32_t ri0 = __builtin_amdgcn_readfirstlane(r.second ? t * (p.heads - p.heads0) + hk : t * p.heads0 + hk);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(div_heads(hp, row0));
+    const uint32_t h0 = row0 - t * hp.heads;
+    r.second = h0 >= hp.heads0;
+    const uint32_t hk = __builtin_amdgcn_readfirstlane(r.second ? h0 - hp.heads0 : h0);  // head inside its tensor
+    const uint32_t ri0 = __builtin_amdgcn_readfirstlane(r.second ? t * (hp.heads - hp.heads0) + hk : t * hp.heads0 + hk);
     r.tok = t;
     r.ri0 = ri0;
     r.ri = ri0 + slot;
     r.row = row0 + slot;
-    r.xoff = (uint64_t)t * (r.second ? p.xs1 : p.xs0) + (uint64_t)hk * D;
+    r.xoff = (uint64_t)t * (r.second ? hp.xs1 : hp.xs0) + (uint64_t)hk * D;
   } else {
     // rows past the end repeat the last row (same inputs, same bytes written)
     const uint32_t row = min(pass * (uint32_t)G + slot, p.total_rows - 1);
     r.row = row;
-    const uint32_t t = div_heads(p, row);
-    const uint32_t h = row - t * p.heads;
+    const uint32_t t = div_heads(hp, row);
+    const uint32_t h = row - t * hp.heads;
     r.tok = t;
-    r.second = h >= p.heads0;
-    const uint32_t hk = r.second ? h - p.heads0 : h;
-    r.ri = r.second ? t * (p.heads - p.heads0) + hk : t * p.heads0 + hk;
+    r.second = h >= hp.heads0;
+    const uint32_t hk = r.second ? h - hp.heads0 : h;
+    r.ri = r.second ? t * (hp.heads - hp.heads0) + hk : t * hp.heads0 + hk;
     r.ri0 = 0;
-    r.xoff = (uint64_t)t * (r.second ? p.xs1 : p.xs0) + (uint64_t)hk * D;
+    r.xoff = (uint64_t)t * (r.second ? hp.xs1 : hp.xs0) + (uint64_t)hk * D;
   }
   r.trow = r.tok;
   if constexpr (POS) {
@@ -168,7 +187,10 @@ __device__ __forceinline__ Loc locate(const RowParams& p, uint32_t pass, uint32_
 }
 
 template <class DT, int L, int MODE, bool ALIGNED, bool MT = false>
-__global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
+__global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x1_or_mt, uint64_t xs0, uint64_t xs1,
+                                                   uint32_t waves, uint32_t passes, uint32_t heads, uint32_t heads0,
+                                                   uint32_t div_magic, uint32_t shift_rope, RowParams p) {
+  const RowHot hp{x0, x1_or_mt, xs0, xs1, waves, passes, heads, heads0, div_magic, shift_rope};
   constexpr bool QUANT = (MODE & ROW_QUANT) != 0;
   constexpr bool ROPE = (MODE & ROW_ROPE) != 0;
   constexpr bool WY = (MODE & ROW_Y) != 0;
@@ -201,12 +223,14 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   // each a full memory latency before the first input load goes out)
   uint32_t blk = blockIdx.x;
   {
-    const uint32_t nb = gridDim.x, full = nb & ~7u;
+    // (the grid's size from the preloaded wave count: the grid size itself is
+    // a kernel argument the hardware does not preload)
+    const uint32_t nb = (hp.waves + RW - 1) / RW, full = nb & ~7u;
     const uint32_t moved = (blk & 7u) * (full >> 3) + (blk >> 3);
     blk = blk < full ? moved : blk;
   }
   const uint32_t gw = blk * RW + wave;
-  const uint32_t W = p.waves, n = p.per_wave, last = p.passes - 1;
+  const uint32_t W = hp.waves, n = p.per_wave, last = hp.passes - 1;
   // (waves past p.waves, at most RW - 1 in the last workgroup, repeat passes of
   // other waves, clamped into range, and write identical bytes: an early exit
   // would be a branch ahead of the kernel-argument loads, see below)
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
 #endif
 
   // ---- this lane's columns
-  const uint32_t R = ROPE ? p.rope : 0u, half = R / 2;
+  const uint32_t R = ROPE ? hp.rope() : 0u, half = R / 2;
   const uint32_t n_plain = (D - R) / 16;  // units outside the rope tail
   const bool rope_lane = u >= n_plain;
   // (selects, not an if / else: no branch ahead of the kernel-argument loads,
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   // several tokens, the row's place inside its token otherwise)
   const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
   uint32_t px0 = slot * D;
-  if constexpr (MT) px0 = (slot >> p.tok_shift) * (uint32_t)p.xs0 + (slot & ((1u << p.tok_shift) - 1u)) * D;
+  if constexpr (MT) px0 = (slot >> hp.tok_shift()) * (uint32_t)hp.xs0 + (slot & ((1u << hp.tok_shift()) - 1u)) * D;
   const uint32_t px_a = px0 + off_a, px_b = px0 + off_b;
   // aligned rope passes: lane l carries bytes [TB l, TB l + TB) of the token's
   // cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB bytes
@@ -239,7 +263,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   constexpr uint32_t TB = MT ? 16u : (D / 32 < 4 ? 4u : (uint32_t)(D / 32));
   const uint32_t toff = TB * lane;
   // the pass's table block: one row, or the rows of its tokens in order
-  const uint32_t tpp = MT ? (uint32_t)G >> p.tok_shift : 1u;  // tokens per pass
+  const uint32_t tpp = MT ? (uint32_t)G >> hp.tok_shift() : 1u;  // tokens per pass
   const uint32_t tbytes = 4u * half * tpp;                      // bytes of the block (cos or sin)
   const bool t_lane = toff < tbytes;
   float* t_wave = t_lds + (STAGED ? wave * TW : 0);
@@ -258,24 +282,28 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
       d.sw = buf_load16(rs, toff);
     }
   };
-  auto load_data = [&](Data& d, uint32_t pass) {
-    d.loc = locate<G, D, ALIGNED, POS, MT>(p, pass, slot);
+  // a pass's input (and, through load_data, its table chunks)
+  auto load_input = [&](Data& d, uint32_t pass) {
+    d.loc = locate<G, D, ALIGNED, POS, MT>(p, hp, pass, slot);
     if constexpr (ALIGNED) {
       // the pass's G rows: one wave-uniform descriptor, lane byte offsets
-      const rsrc_t rx = make_rsrc((d.loc.second ? p.x1 : p.x0) + d.loc.xoff, MT ? p.xspan : 2u * G * D);
+      const rsrc_t rx = make_rsrc((d.loc.second && !MT ? hp.x1() : hp.x0) + d.loc.xoff, MT ? hp.xspan() : 2u * G * D);
       d.xa = buf_load16_nt(rx, 2u * px_a);
       d.xb = buf_load16_nt(rx, 2u * px_b);
-      // the token's cos and sin rows (wave-uniform descriptors), one chunk of
-      // each per lane, in flight with the input: the wait for a pass's input
-      // covers them, and it never waits on the previous pass's stores. (With a
-      // positions index the row number is itself a load: the table chunks then
-      // go out from the middle of the previous pass, see compute.)
-      if constexpr (STAGED && !POS) load_staged_table(d);
     } else {
-      const uint16_t* src = (d.loc.second ? p.x1 : p.x0) + d.loc.xoff;
+      const uint16_t* src = (d.loc.second ? hp.x1() : hp.x0) + d.loc.xoff;
       d.xa = load_stream16(src + off_a);
       d.xb = load_stream16(src + off_b);
     }
+  };
+  auto load_data = [&](Data& d, uint32_t pass) {
+    load_input(d, pass);
+    // the token's cos and sin rows (wave-uniform descriptors), one chunk of
+    // each per lane, in flight with the input: the wait for a pass's input
+    // covers them, and it never waits on the previous pass's stores. (With a
+    // positions index the row number is itself a load: the table chunks then
+    // go out from the middle of the previous pass, see compute.)
+    if constexpr (STAGED && !POS) load_staged_table(d);
   };
   // per-lane rows: every lane loads its own table values (plain lanes read the
   // row start and ignore it); aligned rope passes load theirs with the input
@@ -363,7 +391,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
         float4 c0 = t.c0, c1 = t.c1, s0 = t.s0, s1 = t.s1;
         if constexpr (STAGED) {
           // this row's token inside the pass (0 unless a pass holds several tokens)
-          const uint32_t tb = MT ? (slot >> p.tok_shift) * half : 0u;
+          const uint32_t tb = MT ? (slot >> hp.tok_shift()) * half : 0u;
           const uint32_t sb = tpp * half + tb;
           c0 = *(const float4*)(t_wave + tb + cs_off);
           c1 = *(const float4*)(t_wave + tb + cs_off + 4);
@@ -472,23 +500,38 @@ __global__ __launch_bounds__(RT) void rows_kernel(RowParams p) {
   // ahead, table values one pass ahead (ring slots are compile-time indices).
   Data d[NS];
   Table tb[2];
-  // ---- weights of both tensors: 16-byte chunks (D / 8 per tensor), loaded
-  // before any input so that waiting for them never waits for an input; lane
-  // l loads chunk l % (D / 4) (and l + 64 when D = 512) and stores it in the
-  // wave's slot as fp32
+  // ---- the first passes' input goes out first: its addresses need only the
+  // preloaded arguments. The weights and then the table chunks follow once a
+  // load of the kernel arguments has given their pointers; the weights go to
+  // LDS after that, and waiting for them waits for the input too (the memory
+  // counter is in order), which the first pass needs anyway, but not for the
+  // table chunks issued after them. (Scheduling barriers keep this order: the
+  // scheduler would otherwise hoist the later loads, and the wait for their
+  // pointers, above the input loads.)
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) load_input(d[k], pass_of(k));
+  __builtin_amdgcn_sched_barrier(0);
+  // weights of both tensors: 16-byte chunks (D / 8 per tensor); lane l loads
+  // chunk l % (D / 4) (and l + 64 when D = 512) and stores it in the wave's
+  // slot as fp32
   constexpr uint32_t WCH = D / 4;                     // chunks of both tensors
   constexpr uint32_t WPL = WCH > 64 ? WCH / 64 : 1;   // chunks per lane
   uint4 wc[WPL];
 #pragma unroll
   for (uint32_t i = 0; i < WPL; ++i) {
     const uint32_t c = (lane + 64 * i) % WCH;
-    const uint16_t* src = (c < D / 8 ? p.w0 : (p.heads0 < p.heads ? p.w1 : p.w0)) + 8 * (c % (D / 8));
+    const uint16_t* src = (c < D / 8 ? p.w0 : (hp.heads0 < hp.heads ? p.w1 : p.w0)) + 8 * (c % (D / 8));
     wc[i] = *(const uint4*)src;
   }
+  if constexpr (STAGED) {
+    // (with positions only the first pass's: each later one goes out from the
+    // middle of the pass before it, see compute)
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k) load_data(d[k], pass_of(k));
-  if constexpr (STAGED && POS) load_staged_table(d[0]);
-  if constexpr (!STAGED) load_table(tb[0], d[0].loc);
+    for (int k = 0; k < (POS ? 1 : NS - 1); ++k) load_staged_table(d[k]);
+  } else {
+    load_table(tb[0], d[0].loc);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // (lanes past the chunks store a copy of the same values: no branch around
   // the loads' use, which would let the compiler sink them under it)
 #pragma unroll

@@ -6,18 +6,25 @@
 
 namespace rnq {
 
+// (the fields a wave needs before its first input load go first, as scalar
+// arguments the hardware preloads; passes of whole tokens carry the token
+// shift and input span in the x1 slot)
+#define RNQ_ROWS_HOT(p, mt)                                                                                      \
+  (p).x0, (mt) ? ((uint64_t)(p).xspan << 32 | (p).tok_shift) : (uint64_t)(uintptr_t)(p).x1, (p).xs0, (p).xs1, \
+      (p).waves, (p).passes, (p).heads, (p).heads0, (p).div_magic, (p).div_shift | (p).rope << 8, (p)
+
 template <class DT, int L, int MODE>
 static hipError_t launch_shape(const RowParams& p, int align, dim3 grid, hipStream_t s) {
   if constexpr ((MODE & ROW_POS) == 0) {
     if (align == ROWS_WHOLE_TOKENS) {
-      hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true, true>), grid, dim3(RT), 0, s, p);
+      hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true, true>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, true));
       return hipGetLastError();
     }
   }
   if (align == ROWS_ONE_TOKEN)
-    hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true>), grid, dim3(RT), 0, s, p);
+    hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, false));
   else if (align == ROWS_PER_LANE)
-    hipLaunchKernelGGL((rows_kernel<DT, L, MODE, false>), grid, dim3(RT), 0, s, p);
+    hipLaunchKernelGGL((rows_kernel<DT, L, MODE, false>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, false));
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
