@@ -36,8 +36,31 @@ constexpr uint32_t kMaxRope = 1024;
 // multiply-shift, the launcher gives every call a token stride and the table's
 // row count, and a position-indexed table is a template case; with positions
 // the table row is a second, dependent round, after the input loads.)
+// The fields a workgroup needs before its first loads (its row of x, the
+// weights, the tail's cos / sin values) come as leading scalar arguments, 14
+// dwords that gfx950 preloads into scalar registers at wave launch: a
+// workgroup then issues them without first loading its kernel arguments,
+// which every workgroup (one per row) would otherwise wait for.
+struct GroupHot {
+  const uint16_t* x;
+  uint64_t xs;  // token stride of x in elements
+  const uint16_t* w;
+  const float* cos;
+  const float* sin;
+  uint32_t n_shift_rope;  // N | div_shift << 15 | rope << 21
+  uint32_t rows_per_token, div_magic, table_bytes;
+  __device__ __forceinline__ uint32_t N() const { return n_shift_rope & 0x7fffu; }
+  __device__ __forceinline__ uint32_t div_shift() const { return (n_shift_rope >> 15) & 0x3fu; }
+  __device__ __forceinline__ uint32_t rope() const { return n_shift_rope >> 21; }
+};
+
 template <class DT, int KC, int GL, bool QUANT = true, bool POS = false>
-__global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
+__global__ __launch_bounds__(GT) void group_quant_kernel(const uint16_t* x, uint64_t xs, const uint16_t* w,
+                                                         const float* cos, const float* sin, uint32_t n_shift_rope,
+                                                         uint32_t rows_per_token, uint32_t div_magic,
+                                                         uint32_t table_bytes, GroupQuantParams p) {
+  const GroupHot hp{x, xs, w, cos, sin, n_shift_rope, rows_per_token, div_magic, table_bytes};
+  const uint32_t N = hp.N();
   constexpr uint32_t kOutOfRange = 0x80000000u;
   __shared__ double part[GWV];
   __shared__ float tail_s[kMaxRope];
@@ -45,8 +68,8 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = tid >> 6;
   const uint32_t row = blockIdx.x;
-  const uint32_t nch = p.N / 8;
-  const uint32_t row_bytes = 2u * p.N;
+  const uint32_t nch = N / 8;
+  const uint32_t row_bytes = 2u * N;
 
   uint32_t ch[KC], off[KC];
   bool ok[KC];
@@ -57,10 +80,10 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
     off[k] = ok[k] ? 16u * ch[k] : kOutOfRange;
   }
   // the row's token and its place in a (possibly strided) view
-  const uint32_t tok = (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);
-  const size_t xoff = (size_t)tok * p.xs + (size_t)(row - tok * p.rows_per_token) * p.N;
-  const rsrc_t rx = make_rsrc(p.x + xoff, row_bytes);
-  const rsrc_t rw = make_rsrc(p.w, row_bytes);
+  const uint32_t tok = (uint32_t)(((uint64_t)row * hp.div_magic) >> hp.div_shift());
+  const size_t xoff = (size_t)tok * hp.xs + (size_t)(row - tok * hp.rows_per_token) * N;
+  const rsrc_t rx = make_rsrc(hp.x + xoff, row_bytes);
+  const rsrc_t rw = make_rsrc(hp.w, row_bytes);
   uint4 xr[KC], wr[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
@@ -78,7 +101,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   // the rope tail's cos/sin values go out with the row: a thread's chunks are
   // 256 apart and the tail is at most 128 chunks, so a thread owns at most one
   // tail chunk and needs one set of 8 pair columns (other lanes read nothing)
-  const uint32_t R = p.rope, half = R / 2;
+  const uint32_t R = hp.rope(), half = R / 2;
   const uint32_t t0 = nch - R / 8, hc = R / 16;  // first tail chunk, chunks per half
   uint32_t toff = kOutOfRange;
 #pragma unroll
@@ -87,8 +110,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
       const uint32_t j = ch[k] - t0;
       toff = 4u * (trow * half + 8u * (j < hc ? j : j - hc));
     }
-  const uint32_t table_bytes = R > 0 ? p.max_pos * half * 4u : 0u;
-  const rsrc_t rcos = make_rsrc(p.cos, table_bytes), rsin = make_rsrc(p.sin, table_bytes);
+  const rsrc_t rcos = make_rsrc(hp.cos, hp.table_bytes), rsin = make_rsrc(hp.sin, hp.table_bytes);
   const float4 tc0 = buf_load16f(rcos, toff), tc1 = buf_load16f(rcos, toff + 16u);
   const float4 ts0 = buf_load16f(rsin, toff), ts1 = buf_load16f(rsin, toff + 16u);
 
@@ -108,7 +130,7 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
 #pragma unroll
   for (int v = 1; v < GWV; ++v) tot += part[v];
   const float ssq = (float)tot;            // one rounding of the exact sum
-  const float rstd = rstd_of(ssq / (float)p.N + p.eps);
+  const float rstd = rstd_of(ssq / (float)N + p.eps);
 
   // ---- normalise: (x * rstd) * w, rounded to the input dtype
   float y[KC][8];
@@ -153,15 +175,15 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
   }
 
   if (!QUANT || p.y != nullptr) {
-    const rsrc_t ry = make_rsrc(p.y + (size_t)row * p.N, row_bytes);
+    const rsrc_t ry = make_rsrc(p.y + (size_t)row * N, row_bytes);
 #pragma unroll
     for (int k = 0; k < KC; ++k) buf_store16_nt(ry, off[k], pack8<DT>(y[k]));
   }
   if constexpr (!QUANT) return;
 
   // ---- per-group absmax, scale and codes
-  const uint32_t n_groups = p.N / p.group_size;
-  const rsrc_t rq = make_rsrc(p.codes + (size_t)row * p.N, p.N);
+  const uint32_t n_groups = N / p.group_size;
+  const rsrc_t rq = make_rsrc(p.codes + (size_t)row * N, N);
   const rsrc_t rs = make_rsrc(p.scales + (size_t)row * n_groups, 4u * n_groups);
   float row_amax = 0.0f;
   if constexpr (GL == 0) {
@@ -218,20 +240,25 @@ __global__ __launch_bounds__(GT) void group_quant_kernel(GroupQuantParams p) {
 
 // --------------------------------------------------------------- launcher
 
+// (the leading, preloaded arguments: see GroupHot)
+#define RNQ_GROUP_HOT(p)                                                                                  \
+  (p).x, (p).xs, (p).w, (p).cos, (p).sin, (p).N | (p).div_shift << 15 | (p).rope << 21, (p).rows_per_token, \
+      (p).div_magic, (p).rope > 0 ? (p).max_pos * ((p).rope / 2) * 4u : 0u, (p)
+
 template <class DT, int KC>
 static hipError_t launch_kc(const GroupQuantParams& p, dim3 g, hipStream_t s) {
   if (p.group_size == p.N && (p.N > 512 || (p.N & (p.N - 1)) != 0)) {  // one group per row (not one wave's lanes)
-    hipLaunchKernelGGL((group_quant_kernel<DT, KC, 0>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, KC, 0>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p));
     return hipGetLastError();
   }
   switch (p.group_size / 8) {
-    case 1: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 1>), g, dim3(GT), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 2>), g, dim3(GT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 4>), g, dim3(GT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 8>), g, dim3(GT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 16>), g, dim3(GT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 32>), g, dim3(GT), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 64>), g, dim3(GT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 1>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 2: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 2>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 4: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 4>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 8: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 8>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 16: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 16>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 32: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 32>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
+    case 64: hipLaunchKernelGGL((group_quant_kernel<DT, KC, 64>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p)); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -251,13 +278,13 @@ template <class DT, bool POS>
 static hipError_t launch_norm_rope_dt(const GroupQuantParams& p, dim3 g, hipStream_t s) {
   const uint32_t nch = p.N / 8;
   if (nch <= GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 1, 0, false, POS>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 1, 0, false, POS>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p));
   else if (nch <= 2 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 2, 0, false, POS>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 2, 0, false, POS>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p));
   else if (nch <= 4 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 4, 0, false, POS>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 4, 0, false, POS>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p));
   else if (nch <= 8 * GT)
-    hipLaunchKernelGGL((group_quant_kernel<DT, 8, 0, false, POS>), g, dim3(GT), 0, s, p);
+    hipLaunchKernelGGL((group_quant_kernel<DT, 8, 0, false, POS>), g, dim3(GT), 0, s, RNQ_GROUP_HOT(p));
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
