@@ -35,8 +35,12 @@ constexpr int WW = WT / 64;
 // group repeats row M - 1, writing identical bytes). All its loads are issued
 // at once (buffer accesses, lanes past the row's end out of the descriptor's
 // range); one barrier for the RB rows' sums of squares.
+// (its parameters, 11 dwords, are scalar arguments: gfx950 preloads them, so
+// a workgroup issues its loads without first loading its kernel arguments)
 template <class DT, int KC, int RB>
-__global__ __launch_bounds__(WT) void wide_fwd_kernel(WideFwdParams p) {
+__global__ __launch_bounds__(WT) void wide_fwd_kernel(const uint16_t* x_in, const uint16_t* w_in, uint16_t* y_out,
+                                                      float* rstd_out, uint32_t M, uint32_t N, float eps) {
+  const WideFwdParams p{x_in, w_in, y_out, rstd_out, M, N, eps};
   constexpr uint32_t kOutOfRange = 0x80000000u;
   __shared__ double part[RB][WW];
   const uint32_t tid = threadIdx.x;
@@ -428,10 +432,10 @@ static hipError_t fwd_kc(const WideFwdParams& p, int kc, hipStream_t s) {
   constexpr int B = RNQ_FWD_ROWS;
   const dim3 b(WT);
   switch (kc) {
-    case 1: hipLaunchKernelGGL((wide_fwd_kernel<DT, 1, B>), dim3((p.M + B - 1) / B), b, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((wide_fwd_kernel<DT, 2, B>), dim3((p.M + B - 1) / B), b, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((wide_fwd_kernel<DT, 4, 1>), dim3(p.M), b, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((wide_fwd_kernel<DT, 8, 1>), dim3(p.M), b, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((wide_fwd_kernel<DT, 1, B>), dim3((p.M + B - 1) / B), b, 0, s, p.x, p.w, p.y, p.rstd, p.M, p.N, p.eps); break;
+    case 2: hipLaunchKernelGGL((wide_fwd_kernel<DT, 2, B>), dim3((p.M + B - 1) / B), b, 0, s, p.x, p.w, p.y, p.rstd, p.M, p.N, p.eps); break;
+    case 4: hipLaunchKernelGGL((wide_fwd_kernel<DT, 4, 1>), dim3(p.M), b, 0, s, p.x, p.w, p.y, p.rstd, p.M, p.N, p.eps); break;
+    case 8: hipLaunchKernelGGL((wide_fwd_kernel<DT, 8, 1>), dim3(p.M), b, 0, s, p.x, p.w, p.y, p.rstd, p.M, p.N, p.eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
