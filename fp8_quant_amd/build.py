@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librnq.so")
-SOURCES = ["rnq_api.hip", "rnq_rows.hip", "rnq_rows_quant.hip", "rnq_rows_norm.hip", "rnq_rows_pos.hip", "rnq_wide.hip", "rnq_group.hip", "rnq_narrow_bwd.hip", "rnq_baselines.hip"]
+SOURCES = ["rnq_api.hip", "rnq_rows.hip", "rnq_rows_quant.hip", "rnq_rows_norm.hip", "rnq_rows_pos.hip", "rnq_wide.hip", "rnq_group.hip", "rnq_narrow_bwd.hip", "rnq_row_bwd.hip", "rnq_baselines.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -370,7 +370,8 @@ rnq_status rnq_rmsnorm_rope_fp8_grouped(const void* x, const void* w, const floa
 
 size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
-  const uint32_t blocks = std::max(bwd_blocks(M, N, false), bwd_blocks(M, N, true));
+  // (rope_dim 0, and 1024: past the wave-per-row kernel's tails, the largest partition)
+  const uint32_t blocks = std::max(bwd_blocks(M, N, 0), bwd_blocks(M, N, 1024));
   return (size_t)blocks * (size_t)N * sizeof(float);
 }
 
@@ -458,12 +459,13 @@ static rnq_status rmsnorm_bwd_common(const char* name, const void* x, const void
   for (const void* ptr : a16)
     if (!aligned(ptr, 16)) return fail(RNQ_ERR_UNSUPPORTED, "tensor pointer %p is not 16-byte aligned", ptr);
   if (!aligned(rstd, 4)) return fail(RNQ_ERR_UNSUPPORTED, "rstd must be 4-byte aligned");
-  const uint32_t blocks = bwd_blocks(M, N, rope_dim > 0);
+  const uint32_t blocks = bwd_blocks(M, N, rope_dim);
   const uint32_t rows_per_block = (uint32_t)((M + blocks - 1) / blocks);
-  // the kernels address the tables (and the narrow one a block's rows) with 32-bit offsets
+  // the kernels address the tables (and the narrow and wave-per-row ones a
+  // block's rows) with 32-bit offsets
   const int64_t table_bytes = (M / rows_per_token) * (rope_dim / 2) * 4;
-  if (table_bytes >= ((int64_t)1 << 31) ||
-      (narrow_bwd_width(N) && (int64_t)rows_per_block * N * 2 >= ((int64_t)1 << 31)))
+  if (table_bytes >= ((int64_t)1 << 31) || ((narrow_bwd_width(N) || row_bwd_fits(N, rope_dim)) &&
+                                            (int64_t)rows_per_block * N * 2 >= ((int64_t)1 << 31)))
     return fail(RNQ_ERR_UNSUPPORTED, "a block's rows or the cos/sin table exceed 2 GiB");
   if (use_scratch) {
     const rnq_status ss = scratch_for_stream((hipStream_t)stream, &workspace);

@@ -172,14 +172,17 @@ hipError_t launch_design(const RowParams& p, uint32_t rows_per_block, int D, boo
 // src_bytes / 2048 blocks of the memory-floor kernel (0: one empty workgroup)
 hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s);
 
-// Deterministic row partition used by the backward (rope: the RoPE backward);
-// the workspace size covers the larger of the two.
-uint32_t bwd_blocks(int64_t M, int64_t N, bool rope);
+// Deterministic row partition used by the backward (rope_dim > 0: the RoPE
+// backward); the workspace size covers every rope_dim.
+uint32_t bwd_blocks(int64_t M, int64_t N, int64_t rope_dim);
 hipError_t launch_wide_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
 // grad_w[j] = sum over b of partial[b, j] in a fixed order
 hipError_t launch_dw_reduce(const float* partial, float* gw, uint32_t blocks, uint32_t N, hipStream_t stream);
 // rows of 64, 128, 256 or 512 elements, several per wave; rope optional
 bool narrow_bwd_width(int64_t N);
 hipError_t launch_narrow_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
+// rows of 1024, 2048 or 4096 elements, one wave per row; rope at most 512
+bool row_bwd_fits(int64_t N, int64_t rope_dim);
+hipError_t launch_row_bwd(WideBwdParams p, bool bf16, hipStream_t stream);
 
 }  // namespace rnq

@@ -487,20 +487,23 @@ hipError_t launch_wide_fwd(const WideFwdParams& p, bool bf16, hipStream_t stream
 }
 
 // Blocks of contiguous rows, every block owning at least one row: about 256
-// (one workgroup per CU), or 512 (two) for the RoPE backward up to 8192 rows.
-// At 4096 x 4096: the plain backward 24.8 us with 256 blocks against 26.0 with
-// 512 (half the partial rows of grad_w to write and read back), the RoPE
-// backward 27.9 us with 512 against 30.5 with 256 (its per-batch LDS exchange
-// of the tail needs the second workgroup's waves to hide behind).
-uint32_t bwd_blocks(int64_t M, int64_t N, bool rope) {
-  (void)N;
+// (one workgroup per CU), or 512 (two) for the RoPE backward of the
+// workgroup-per-row kernel up to 8192 rows. At 4096 x 4096 that kernel's plain
+// backward took 24.8 us with 256 blocks against 26.0 with 512 (half the
+// partial rows of grad_w to write and read back), its RoPE backward 27.9 us
+// with 512 against 30.5 with 256 (its per-batch LDS exchange of the tail needs
+// the second workgroup's waves to hide behind). The wave-per-row kernel holds
+// one workgroup per CU (its LDS) and takes 256 either way.
+uint32_t bwd_blocks(int64_t M, int64_t N, int64_t rope_dim) {
   if (M <= 0) return 1;
-  const int64_t target = rope && M <= 8192 ? 512 : 256;
+  const bool two_per_cu = rope_dim > 0 && M <= 8192 && !row_bwd_fits(N, rope_dim);
+  const int64_t target = two_per_cu ? 512 : 256;
   const int64_t rpb = (M + target - 1) / target;
   return (uint32_t)((M + rpb - 1) / rpb);
 }
 
 hipError_t launch_wide_bwd(WideBwdParams p, bool bf16, hipStream_t stream) {
+  if (row_bwd_fits(p.N, p.rope)) return launch_row_bwd(p, bf16, stream);
   dim3 grid(p.blocks);
   const int kc = chunks_per_lane(p.N, p.N > 2048 ? 512 : 256);
   if (p.rope > kMaxBwdRope || p.rope % 16 != 0 || p.rope > p.N) return hipErrorInvalidValue;

@@ -125,7 +125,7 @@ def test_rmsnorm_argument_validation():
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 6, 4096, 2048, 1, 1e-6, 0, None) == 3  # tail > 1024
     assert lib.rnq_rmsnorm_rope(FAKE, FAKE, None, None, FAKE, 6, 4096, 64, 1, 1e-6, 0, None) == 1  # wide rows, no table
     need = lib.rnq_rmsnorm_bwd_workspace_size(4096, 4096)
-    assert need == 512 * 4096 * 4  # the RoPE backward's 512 blocks of 8 rows (the plain one takes 256 of 16)
+    assert need == 512 * 4096 * 4  # 512 blocks of 8 rows: the RoPE backward with a tail above 512 columns
     assert lib.rnq_rmsnorm_bwd_workspace_size(16384, 4096) == 256 * 4096 * 4
     assert lib.rnq_rmsnorm_bwd_workspace_size(257, 1024) == 257 * 1024 * 4  # one row per block (RoPE partition)
     assert lib.rnq_rmsnorm_bwd_workspace_size(0, 4096) == 0

@@ -181,6 +181,30 @@ def test_autograd_only_weight_grad():
     assert np.abs(dw - ref_dw).max() <= 2e-2 * (np.abs(ref_dw).max() + 1e-30)
 
 
+# ------------------------------- rows of 1024, 2048 and 4096: one wave per row
+
+ROW = [
+    # M, N, R, dtype, rows_per_token, saved rstd
+    (1, 1024, 0, torch.bfloat16, 1, False),    # one row: one wave of one block
+    (9, 1024, 16, torch.float16, 1, True),     # the narrowest tail
+    (300, 2048, 64, torch.bfloat16, 3, False),
+    (1000, 2048, 0, torch.float16, 1, True),   # 4 rows per block: waves 4..7 without a row
+    (777, 4096, 256, torch.float16, 1, False),
+    (2100, 4096, 512, torch.bfloat16, 7, True),  # the widest tail these rows take (every lane of the last slot)
+    (4096, 1024, 128, torch.bfloat16, 8, False),
+]
+
+
+@pytest.mark.parametrize("M,N,R,dtype,rpt,saved", ROW, ids=[f"{m}x{n}r{r}" for m, n, r, _, _, _ in ROW])
+def test_row_bwd_shapes(M, N, R, dtype, rpt, saved):
+    """Rows of 1024, 2048 and 4096 elements with tails up to 512 columns go
+    through the wave-per-row backward: ragged row counts leave the waves of a
+    block with no row, one row or several; saved and recomputed rstd."""
+    x, w, gy, cos, sin = _case(M, N, R, seed=5 * M + N + R, dtype=dtype, rows_per_token=rpt)
+    rstd = rnq.rmsnorm(gpu(x), gpu(w), return_rstd=True)[1] if saved else None
+    _rope_bwd(f"row bwd M{M} N{N} R{R} {DT[dtype]} saved {saved}", x, w, gy, cos, sin, rpt, rstd)
+
+
 # ------------------------------------------- grad_w: every row counted exactly once
 
 EDGE = [
@@ -189,7 +213,9 @@ EDGE = [
     (4100, 2048, 0, torch.bfloat16, 1),     # ragged: 242 blocks of 17 rows, the last one of 3
     (16384, 128, 0, torch.float16, 1),      # narrow rows: 256 blocks of 64
     (16384, 128, 64, torch.float16, 1),     # narrow rows through the RoPE backward: 256 blocks of 64
-    (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward: 512 blocks of 4
+    (2048, 4096, 128, torch.bfloat16, 2),   # wide rows through the RoPE backward: 256 blocks of 8
+    (3000, 4096, 512, torch.bfloat16, 3),   # 250 blocks of 12: waves 0..3 take two rows, 4..7 one
+    (2000, 8192, 128, torch.bfloat16, 1),   # workgroup-per-row RoPE backward: 500 blocks of 4
     (20000, 256, 0, torch.bfloat16, 1),     # 254 blocks of 79, the last one of 13
 ]
 
@@ -202,8 +228,11 @@ def test_grad_w_counts_block_edge_rows_once(M, N, R, dtype, rpt):
     reduction moves a column of grad_w by a whole row's gy * xn, which the
     per-column bound 1e-4 * sum over rows of |gy * xn| catches (the 2e-2 rule
     of the full-size tests cannot see one row out of thousands)."""
-    # the partition: about 256 blocks, or 512 for the RoPE backward up to 8192 rows
-    target = 512 if (R and M <= 8192) else 256
+    # the partition: about 256 blocks, or 512 for the RoPE backward up to 8192
+    # rows when it runs a workgroup per row (rows other than 64..512, 1024,
+    # 2048 and 4096 wide, or tails above 512 columns)
+    wave_per_row = N in (1024, 2048, 4096) and R <= 512
+    target = 512 if (R and M <= 8192 and not wave_per_row) else 256
     rpb = -(-M // target)
     blocks = -(-M // rpb)
     picks = sorted({r for b in (0, blocks // 2, blocks - 1) for r in (b * rpb, min(b * rpb + rpb, M) - 1)} | {M - 1})

@@ -20,10 +20,11 @@ import sys
 
 import pytest
 
+from fp8_quant_amd import build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp8_quant_amd", "csrc")
-SOURCES = ["rnq_api", "rnq_rows", "rnq_rows_quant", "rnq_rows_norm", "rnq_rows_pos", "rnq_wide", "rnq_group",
-           "rnq_narrow_bwd", "rnq_baselines"]
+SOURCES = [s[: -len(".hip")] for s in build.SOURCES]  # every unit of the library
 SAN_ENV = {"ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1:abort_on_error=0",
            "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
 
