@@ -625,13 +625,19 @@ def main() -> int:
         paths = []
         steps, warm = max(10, args.steps // 4), max(2, args.warmup // 4)
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_small", steps, warm)))
-        paths += [_summary(r) for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, warm)]
+        # (every path but the small ones with the memory floor for its own byte count, timed in this run)
+        paths += [_with_floor(torch, _summary(r), steps, warm)
+                  for r in bench_rmsnorm(torch, rnq, workloads, ledger, "rmsnorm_4k", steps, warm)]
         paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_fp16",
                                                                  steps, warm)), steps, warm))
-        paths.append(_summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)))
-        paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps, warm)))
-        paths.append(_summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_4k", steps, warm)))
-        paths.append(_summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_4k", steps, warm)))
+        paths.append(_with_floor(torch, _summary(bench_grouped(torch, rnq, workloads, ledger, "grouped_4k", steps, warm)),
+                                 steps, warm))
+        paths.append(_with_floor(torch, _summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_fp16", steps,
+                                                                warm)), steps, warm))
+        paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_4k", steps,
+                                                                 warm)), steps, warm))
+        paths.append(_with_floor(torch, _summary(bench_rope_bwd(torch, rnq, workloads, ledger, "norm_rope_4k", steps,
+                                                                warm)), steps, warm))
         paths.append(_summary(bench_qk(torch, rnq, workloads, ledger, "qk_4k_fused", steps, warm)))
         paths.append(_with_floor(torch, _summary(bench_norm_rope(torch, rnq, workloads, ledger, "norm_rope_pos",
                                                                  steps, warm)), steps, warm))
