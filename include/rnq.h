@@ -102,6 +102,9 @@ size_t rnq_rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
  * a fixed order; results are bitwise reproducible for a given (M, N).
  * workspace_bytes must be >= rnq_rmsnorm_bwd_workspace_size(M, N); the
  * workspace is scratch owned by the caller (16-byte aligned).
+ * Requirements: N a multiple of 8, at most 16384; M < 2^31; for N of 64..512,
+ * 1024, 2048 or 4096 one partition block's rows (about M / 256 rows of x)
+ * below 2 GiB (UNSUPPORTED otherwise).
  */
 rnq_status rnq_rmsnorm_bwd(const void* x, const void* w, const void* grad_y, const float* rstd,
                            void* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
@@ -156,8 +159,10 @@ rnq_status rnq_rmsnorm_rope_ex(const void* x, int64_t x_token_stride, const void
  * cos, sin and rows_per_token those of rnq_rmsnorm_rope.
  * Requirements: N a multiple of 8, at most 16384 (the widths rnq_rmsnorm_bwd
  * takes); R a multiple of 16 with R <= N, and R <= 1024 unless N is 64, 128,
- * 256 or 512; M % rows_per_token == 0; the cos/sin table below 2 GiB. cos/sin
- * may be NULL when R == 0.
+ * 256 or 512; M % rows_per_token == 0; M < 2^31; the cos/sin table below
+ * 2 GiB, and for N of 64..512, or 1024, 2048, 4096 with R <= 512, one
+ * partition block's rows (about M / 256 rows of x) below 2 GiB
+ * (UNSUPPORTED otherwise). cos/sin may be NULL when R == 0.
  */
 rnq_status rnq_rmsnorm_rope_bwd(const void* x, const void* w, const void* grad_y, const float* cos,
                                 const float* sin, const float* rstd, void* grad_x, float* grad_w,
