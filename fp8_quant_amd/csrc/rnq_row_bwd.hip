@@ -46,7 +46,9 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
   constexpr uint32_t row_bytes = 2u * N;
   constexpr uint32_t kOutOfRange = 0x80000000u;
   const uint32_t div_shift = shift_rope & 0xffu, rope = shift_rope >> 8;
-  __shared__ uint4 w_s[N / 8];  // the weight row (16-bit values)
+  // the weight row as fp32 (read where it is used, twice per row, without
+  // unpacking): float4 (2 k + h) * 64 + lane holds columns 8 (lane + 64 k) + 4 h .. + 3
+  __shared__ float4 w_f[N / 4];
   // grad_w sums of each wave: float4 (2 k + h) * 64 + lane of wave v holds
   // columns 8 (lane + 64 k) + 4 h .. + 3 (lanes 16 bytes apart)
   __shared__ float4 dw_s[RBW][N / 4];
@@ -138,6 +140,10 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
       asm volatile("" : "+v"(in.g[k].x), "+v"(in.g[k].y), "+v"(in.g[k].z), "+v"(in.g[k].w));
     }
   };
+  auto wk = [&](int k, float* w) {
+    const float4 a = w_f[(2 * k) * 64 + lane], b = w_f[(2 * k + 1) * 64 + lane];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  };
   auto compute = [&](uint32_t j, In& in) {
     const uint32_t lr = row_of(j);
     float rstd;
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
       float xf[8], gf[8], w[8];
       unpack8<DT>(in.x[k], xf);
       grad(k, gf);
-      unpack8<DT>(w_s[lane + 64 * k], w);
+      wk(k, w);
       dot[k] = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot[k] += (gf[i] * w[i]) * (xf[i] * rstd);
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
       float xf[8], gf[8], w[8], o[8], d[8];
       unpack8<DT>(in.x[k], xf);
       grad(k, gf);
-      unpack8<DT>(w_s[lane + 64 * k], w);
+      wk(k, w);
       const float4 d0 = dw_w[(2 * k) * 64 + lane], d1 = dw_w[(2 * k + 1) * 64 + lane];
       d[0] = d0.x; d[1] = d0.y; d[2] = d0.z; d[3] = d0.w;
       d[4] = d1.x; d[5] = d1.y; d[6] = d1.z; d[7] = d1.w;
@@ -240,8 +246,15 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
   rdx = make_rsrc(p.gx + (size_t)r0 * N, span);
   rrs = make_rsrc(p.rstd + r0, SAVED ? 4u * nrows : 0u);
   load_rs(0, a);
-  // the weight row goes to LDS once the first row's loads are out
-  if (tid < N / 8) w_s[tid] = wc;
+  // the weight row goes to LDS once the first row's loads are out (thread t
+  // holds chunk t = lane + 64 k)
+  if (tid < N / 8) {
+    float wf8[8];
+    unpack8<DT>(wc, wf8);
+    const uint32_t kk = tid / 64, ll = tid % 64;
+    w_f[(2 * kk) * 64 + ll] = make_float4(wf8[0], wf8[1], wf8[2], wf8[3]);
+    w_f[(2 * kk + 1) * 64 + ll] = make_float4(wf8[4], wf8[5], wf8[6], wf8[7]);
+  }
   lds_barrier();
   uint32_t s = 0;
   for (; s + 2 <= mine; s += 2) {
