@@ -102,3 +102,36 @@ def test_rope_bwd_random_shapes(seed):
     err = np.abs(dx - ref_dx) / (np.abs(ref_dx) + np.sqrt((ref_dx**2).mean(axis=1, keepdims=True)))
     errw = np.abs(gw.cpu().numpy() - ref_dw) / (np.abs(ref_dw) + np.sqrt((ref_dw**2).mean()))
     assert err.max() <= 2e-2 and errw.max() <= 2e-2, (err.max(), errw.max())
+
+
+@pytest.mark.parametrize("seed", SEEDS[:8])
+def test_wide_bwd_random_shapes(seed):
+    """Rows wider than a head: 1024, 2048 and 4096 go through the wave-per-row
+    backward when the tail is at most 512 columns, other widths and wider tails
+    through the workgroup-per-row one; saved or recomputed rstd."""
+    rng = np.random.default_rng(4000 + seed)
+    N = int(rng.choice([1024, 2048, 4096, 4096, 1536, 3000, 8192]))
+    R = int(rng.choice([r for r in (0, 16, 64, 128, 512, 1024) if r <= N]))
+    rpt = int(rng.choice([1, 2, 5]))
+    M = rpt * int(rng.integers(1, max(2, 600 // rpt)))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float16
+    saved = bool(rng.random() < 0.4)
+    g = torch.Generator("cpu").manual_seed(100 + seed)
+    x = (torch.randn(M, N, generator=g) * float(rng.choice([0.1, 1.0, 4.0]))).to(dtype)
+    w = (1 + 0.2 * torch.randn(N, generator=g)).to(dtype)
+    gy = torch.randn(M, N, generator=g).to(dtype)
+    cos, sin = workloads.rope_table(rng.integers(0, 5000, M // rpt), R, 10000.0)
+    print(f"[sweep] wide bwd seed {seed}: x({M}, {N}) rope {R} rows/token {rpt} {DT[dtype]} saved {saved}",
+          flush=True)
+    xd, wd = gpu(x), gpu(w)
+    rstd = rnq.rmsnorm(xd, wd, return_rstd=True)[1] if saved else None
+    gx, gw = rnq.rmsnorm_rope_bwd(xd, wd, gpu(gy), gpu(torch.from_numpy(cos)), gpu(torch.from_numpy(sin)), rstd,
+                                  rows_per_token=rpt)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw, _ = oracle.rmsnorm_rope_bwd(workloads.bits(x), workloads.bits(w), workloads.bits(gy), cos, sin,
+                                                1e-6, DT[dtype], rpt)
+    from oracle import codecs
+    dx = codecs.dtype_to_f32(workloads.bits(gx), DT[dtype]).astype(np.float64)
+    err = np.abs(dx - ref_dx) / (np.abs(ref_dx) + np.sqrt((ref_dx**2).mean(axis=1, keepdims=True)))
+    errw = np.abs(gw.cpu().numpy() - ref_dw) / (np.abs(ref_dw) + np.sqrt((ref_dw**2).mean()))
+    assert err.max() <= 2e-2 and errw.max() <= 2e-2, (err.max(), errw.max())
