@@ -106,19 +106,29 @@ struct Table {
 // as leading scalar arguments (14 dwords), which gfx950 preloads into scalar
 // registers at wave launch: the first input loads then go out without
 // waiting for a load of the kernel arguments (one memory latency per launch).
-// On passes of whole tokens (one tensor, no x1) the x1 slot carries the token
-// shift and the pass's input span instead.
+// On passes of whole tokens (one tensor) the slots that only the two-tensor
+// layout needs carry what such a pass needs before its first compute: the
+// weight, cos and sin pointers (the first pass's weights and table rows then
+// go out with its input, not a kernel-argument load later), the pass's input
+// span and the token shift:
+//   x1_or_mt = w0 (low half) | xspan << 32, xs1 = cos, heads | heads0 << 32 =
+//   sin, div_magic = w0 >> 32, and the token shift in div_shift's byte.
 struct RowHot {
   const uint16_t* x0;
-  uint64_t x1_or_mt;  // x1, or tok_shift | xspan << 32
-  uint64_t xs0, xs1;
+  uint64_t x1_or_mt;  // x1, or (uint32_t)w0 | xspan << 32
+  uint64_t xs0, xs1;  // xs1: cos on passes of whole tokens
   uint32_t waves, passes, heads, heads0, div_magic;
-  uint32_t shift_rope;  // div_shift | rope << 8
+  uint32_t shift_rope;  // div_shift (or tok_shift) | rope << 8
   __device__ __forceinline__ uint32_t div_shift() const { return shift_rope & 0xffu; }
   __device__ __forceinline__ uint32_t rope() const { return shift_rope >> 8; }
   __device__ __forceinline__ const uint16_t* x1() const { return (const uint16_t*)x1_or_mt; }
-  __device__ __forceinline__ uint32_t tok_shift() const { return (uint32_t)x1_or_mt; }
+  __device__ __forceinline__ uint32_t tok_shift() const { return shift_rope & 0xffu; }
   __device__ __forceinline__ uint32_t xspan() const { return (uint32_t)(x1_or_mt >> 32); }
+  __device__ __forceinline__ const uint16_t* mt_w0() const {
+    return (const uint16_t*)((uint64_t)div_magic << 32 | (uint32_t)x1_or_mt);
+  }
+  __device__ __forceinline__ const float* mt_cos() const { return (const float*)xs1; }
+  __device__ __forceinline__ const float* mt_sin() const { return (const float*)((uint64_t)heads0 << 32 | heads); }
 };
 
 __device__ __forceinline__ uint32_t div_heads(const RowHot& h, uint32_t row) {
@@ -267,10 +277,13 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   const uint32_t tbytes = 4u * half * tpp;                      // bytes of the block (cos or sin)
   const bool t_lane = toff < tbytes;
   float* t_wave = t_lds + (STAGED ? wave * TW : 0);
+  // (passes of whole tokens: from the preloaded arguments)
+  const float* const cos_tab = MT ? hp.mt_cos() : p.cos;
+  const float* const sin_tab = MT ? hp.mt_sin() : p.sin;
 
   auto load_staged_table = [&](Data& d) {
-    const rsrc_t rc = make_rsrc(p.cos + (size_t)d.loc.trow * half, tbytes);
-    const rsrc_t rs = make_rsrc(p.sin + (size_t)d.loc.trow * half, tbytes);
+    const rsrc_t rc = make_rsrc(cos_tab + (size_t)d.loc.trow * half, tbytes);
+    const rsrc_t rs = make_rsrc(sin_tab + (size_t)d.loc.trow * half, tbytes);
     if constexpr (TB == 4) {
       d.cw.x = buf_load4(rc, toff);
       d.sw.x = buf_load4(rs, toff);
@@ -520,8 +533,15 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
 #pragma unroll
   for (uint32_t i = 0; i < WPL; ++i) {
     const uint32_t c = (lane + 64 * i) % WCH;
-    const uint16_t* src = (c < D / 8 ? p.w0 : (hp.heads0 < hp.heads ? p.w1 : p.w0)) + 8 * (c % (D / 8));
-    wc[i] = *(const uint4*)src;
+    if constexpr (MT) {
+      // (a buffer load: the pointer rebuilt from preloaded integers is generic,
+      // and a flat load's wait would also take the table loads and the
+      // kernel-argument loads issued after it)
+      wc[i] = buf_load16(make_rsrc(hp.mt_w0(), 2u * D), 16u * (c % (D / 8)));
+    } else {
+      const uint16_t* src = (c < D / 8 ? p.w0 : (hp.heads0 < hp.heads ? p.w1 : p.w0)) + 8 * (c % (D / 8));
+      wc[i] = *(const uint4*)src;
+    }
   }
   if constexpr (STAGED) {
     // (with positions only the first pass's: each later one goes out from the

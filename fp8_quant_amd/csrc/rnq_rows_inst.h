@@ -7,11 +7,15 @@
 namespace rnq {
 
 // (the fields a wave needs before its first input load go first, as scalar
-// arguments the hardware preloads; passes of whole tokens carry the token
-// shift and input span in the x1 slot)
-#define RNQ_ROWS_HOT(p, mt)                                                                                      \
-  (p).x0, (mt) ? ((uint64_t)(p).xspan << 32 | (p).tok_shift) : (uint64_t)(uintptr_t)(p).x1, (p).xs0, (p).xs1, \
-      (p).waves, (p).passes, (p).heads, (p).heads0, (p).div_magic, (p).div_shift | (p).rope << 8, (p)
+// arguments the hardware preloads; on passes of whole tokens the slots of the
+// second tensor and of the head division carry the weight, cos and sin
+// pointers, the input span and the token shift, as RowHot lays out)
+#define RNQ_ROWS_HOT(p, mt)                                                                                     \
+  (p).x0,                                                                                                       \
+      (mt) ? ((uint64_t)(p).xspan << 32 | (uint32_t)(uintptr_t)(p).w0) : (uint64_t)(uintptr_t)(p).x1, (p).xs0, \
+      (mt) ? (uint64_t)(uintptr_t)(p).cos : (p).xs1, (p).waves, (p).passes,                                     \
+      (mt) ? (uint32_t)(uintptr_t)(p).sin : (p).heads, (mt) ? (uint32_t)((uintptr_t)(p).sin >> 32) : (p).heads0, \
+      (mt) ? (uint32_t)((uintptr_t)(p).w0 >> 32) : (p).div_magic, ((mt) ? (p).tok_shift : (p).div_shift) | (p).rope << 8, (p)
 
 template <class DT, int L, int MODE>
 static hipError_t launch_shape(const RowParams& p, int align, dim3 grid, hipStream_t s) {
