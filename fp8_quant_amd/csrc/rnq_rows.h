@@ -34,9 +34,10 @@
 //    multiple of the heads per token: one row per token of path R, the
 //    RMSNorm forward, a single-tensor prologue), the same holds with the
 //    pass's first token as the base: the rows of its G / heads tokens sit at
-//    lane-constant offsets, and their table rows are one contiguous block
-//    (16 bytes per lane, staged through LDS like a token's row). Otherwise each
-//    lane locates its own row.
+//    lane-constant offsets, their table rows are consecutive, and each rope
+//    lane loads its own row's 8 cos and 8 sin values with the pass's input (the
+//    rows of such a pass have tokens of their own: nothing to share through
+//    LDS). Otherwise each lane locates its own row.
 //  * Inputs may be views: the rows of a token are contiguous in each input
 //    tensor, and consecutive tokens are xs0 / xs1 elements apart (q and k
 //    inside a fused QKV projection output). Outputs are contiguous.
@@ -93,13 +94,14 @@ struct Loc {
 
 // A pass's input chunks (and, on aligned rope passes, this lane's piece of the
 // token's cos and sin rows, loaded with them: the first 4, 8 or 16 bytes).
+struct Table {
+  float4 c0, c1, s0, s1;  // this lane's values (per-lane rows, and passes of whole tokens)
+};
 struct Data {
   Loc loc;
   uint4 xa, xb;
   uint4 cw, sw;
-};
-struct Table {
-  float4 c0, c1, s0, s1;  // this lane's values (per-lane rows)
+  Table tab;  // passes of whole tokens: this lane's cos / sin values, loaded with the input
 };
 
 // The fields a wave needs before its first input load. They reach the kernel
@@ -213,10 +215,13 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // pass's input has arrived (a barrier made every wave wait for the slowest
   // first input of its workgroup)
   __shared__ float w_lds[RW * 2 * D];
-  // aligned rope passes: each wave stages the pass's cos and sin rows here
-  // (several tokens' rows, at most 1 KB of each, when a pass holds whole tokens)
-  constexpr bool STAGED = ALIGNED && ROPE;
-  constexpr int TW = MT ? (D > 512 ? D : 512) : D;  // floats per wave
+  // passes inside one token: each wave stages the token's cos and sin rows
+  // here (every row of the pass uses the same row); on passes of whole tokens
+  // every row has a token of its own and its rope lanes load their values
+  // directly, with the pass's input (DIRECT)
+  constexpr bool STAGED = ALIGNED && ROPE && !MT;
+  constexpr bool DIRECT = MT && ROPE;
+  constexpr int TW = D;  // floats per wave
   __shared__ float t_lds[STAGED ? RW * TW : 1];
 
   const uint32_t tid = threadIdx.x;
@@ -267,10 +272,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   uint32_t px0 = slot * D;
   if constexpr (MT) px0 = (slot >> hp.tok_shift()) * (uint32_t)hp.xs0 + (slot & ((1u << hp.tok_shift()) - 1u)) * D;
   const uint32_t px_a = px0 + off_a, px_b = px0 + off_b;
-  // aligned rope passes: lane l carries bytes [TB l, TB l + TB) of the token's
-  // cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB bytes
-  // cover it, each byte read once; lanes past the row read zero)
-  constexpr uint32_t TB = MT ? 16u : (D / 32 < 4 ? 4u : (uint32_t)(D / 32));
+  // passes inside one token: lane l carries bytes [TB l, TB l + TB) of the
+  // token's cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB
+  // bytes cover it, each byte read once; lanes past the row read zero)
+  constexpr uint32_t TB = D / 32 < 4 ? 4u : (uint32_t)(D / 32);
   const uint32_t toff = TB * lane;
   // the pass's table block: one row, or the rows of its tokens in order
   const uint32_t tpp = MT ? (uint32_t)G >> hp.tok_shift() : 1u;  // tokens per pass
@@ -295,6 +300,18 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
       d.sw = buf_load16(rs, toff);
     }
   };
+  // passes of whole tokens: a rope lane's 8 cos and 8 sin values, from its
+  // row's token (the pass's tokens are consecutive table rows); plain lanes
+  // read outside the block (zero, no memory access)
+  auto load_direct_table = [&](Data& d) {
+    const rsrc_t rc = make_rsrc(cos_tab + (size_t)d.loc.trow * half, tbytes);
+    const rsrc_t rs = make_rsrc(sin_tab + (size_t)d.loc.trow * half, tbytes);
+    const uint32_t o = rope_lane ? 4u * ((slot >> hp.tok_shift()) * half + cs_off) : 0x80000000u;
+    d.tab.c0 = buf_load16f(rc, o);
+    d.tab.c1 = buf_load16f(rc, o + 16u);
+    d.tab.s0 = buf_load16f(rs, o);
+    d.tab.s1 = buf_load16f(rs, o + 16u);
+  };
   // a pass's input (and, through load_data, its table chunks)
   auto load_input = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, D, ALIGNED, POS, MT>(p, hp, pass, slot);
@@ -317,6 +334,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     // positions index the row number is itself a load: the table chunks then
     // go out from the middle of the previous pass, see compute.)
     if constexpr (STAGED && !POS) load_staged_table(d);
+    if constexpr (DIRECT) load_direct_table(d);
   };
   // per-lane rows: every lane loads its own table values (plain lanes read the
   // row start and ignore it); aligned rope passes load theirs with the input
@@ -382,8 +400,8 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
       // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
       // accesses complete in order, so the reads below see these writes and the
       // previous pass's reads are done before they land
-      // (cos block, then sin block: tpp * half floats each)
-      const uint32_t sin_at = tpp * half;
+      // (the cos row, then the sin row: half floats each)
+      const uint32_t sin_at = half;
       if (t_lane) {
         if constexpr (TB == 4) {
           t_wave[lane] = __uint_as_float(s.cw.x);
@@ -402,12 +420,12 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     if constexpr (ROPE) {
       if (FULL || rope_lane) {
         float4 c0 = t.c0, c1 = t.c1, s0 = t.s0, s1 = t.s1;
-        if constexpr (STAGED) {
-          // this row's token inside the pass (0 unless a pass holds several tokens)
-          const uint32_t tb = MT ? (slot >> hp.tok_shift()) * half : 0u;
-          const uint32_t sb = tpp * half + tb;
-          c0 = *(const float4*)(t_wave + tb + cs_off);
-          c1 = *(const float4*)(t_wave + tb + cs_off + 4);
+        if constexpr (DIRECT) {
+          c0 = s.tab.c0, c1 = s.tab.c1, s0 = s.tab.s0, s1 = s.tab.s1;
+        } else if constexpr (STAGED) {
+          const uint32_t sb = half;
+          c0 = *(const float4*)(t_wave + cs_off);
+          c1 = *(const float4*)(t_wave + cs_off + 4);
           s0 = *(const float4*)(t_wave + sb + cs_off);
           s1 = *(const float4*)(t_wave + sb + cs_off + 4);
         }
@@ -548,6 +566,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     // middle of the pass before it, see compute)
 #pragma unroll
     for (int k = 0; k < (POS ? 1 : NS - 1); ++k) load_staged_table(d[k]);
+  } else if constexpr (DIRECT) {
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) load_direct_table(d[k]);
   } else {
     load_table(tb[0], d[0].loc);
   }
