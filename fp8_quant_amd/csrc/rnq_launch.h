@@ -46,7 +46,6 @@ struct RowParams {
   uint32_t div_magic;
   uint32_t div_shift;
   uint32_t tok_shift;  // passes of whole tokens: log2(heads per token)
-  uint32_t xspan;      // passes of whole tokens: bytes one pass's input rows span
   uint32_t prio_by_progress;  // every wave resident at once: issue priority by passes done
 };
 

@@ -52,6 +52,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "rnq_device.h"
 #include "rnq_launch.h"
 
@@ -101,7 +103,8 @@ struct Data {
   Loc loc;
   uint4 xa, xb;
   uint4 cw, sw;
-  Table tab;  // passes of whole tokens: this lane's cos / sin values, loaded with the input
+  Table tab;     // passes of whole tokens: this lane's cos / sin values
+  uint32_t pos;  // passes of whole tokens with positions: this lane's token's position
 };
 
 // The fields a wave needs before its first input load. They reach the kernel
@@ -109,28 +112,29 @@ struct Data {
 // registers at wave launch: the first input loads then go out without
 // waiting for a load of the kernel arguments (one memory latency per launch).
 // On passes of whole tokens (one tensor) the slots that only the two-tensor
-// layout needs carry what such a pass needs before its first compute: the
-// weight, cos and sin pointers (the first pass's weights and table rows then
-// go out with its input, not a kernel-argument load later), the pass's input
-// span and the token shift:
-//   x1_or_mt = w0 (low half) | xspan << 32, xs1 = cos, heads | heads0 << 32 =
-//   sin, div_magic = w0 >> 32, and the token shift in div_shift's byte.
+// layout and the head division need carry what such a pass needs before its
+// first compute, so that the first pass's weights, positions and table rows go
+// out with its input instead of after a load of the kernel arguments:
+//   x1_or_mt = w0, xs0 = cos, xs1 = sin, heads | heads0 << 32 = positions,
+//   div_magic = the token stride in elements (below 2^30 there), and the token
+//   shift (log2 of the rows per token) in div_shift's byte.
 struct RowHot {
   const uint16_t* x0;
-  uint64_t x1_or_mt;  // x1, or (uint32_t)w0 | xspan << 32
-  uint64_t xs0, xs1;  // xs1: cos on passes of whole tokens
+  uint64_t x1_or_mt;  // x1, or w0 on passes of whole tokens
+  uint64_t xs0, xs1;  // token strides, or cos and sin on passes of whole tokens
   uint32_t waves, passes, heads, heads0, div_magic;
   uint32_t shift_rope;  // div_shift (or tok_shift) | rope << 8
   __device__ __forceinline__ uint32_t div_shift() const { return shift_rope & 0xffu; }
   __device__ __forceinline__ uint32_t rope() const { return shift_rope >> 8; }
   __device__ __forceinline__ const uint16_t* x1() const { return (const uint16_t*)x1_or_mt; }
   __device__ __forceinline__ uint32_t tok_shift() const { return shift_rope & 0xffu; }
-  __device__ __forceinline__ uint32_t xspan() const { return (uint32_t)(x1_or_mt >> 32); }
-  __device__ __forceinline__ const uint16_t* mt_w0() const {
-    return (const uint16_t*)((uint64_t)div_magic << 32 | (uint32_t)x1_or_mt);
+  __device__ __forceinline__ const uint16_t* mt_w0() const { return (const uint16_t*)x1_or_mt; }
+  __device__ __forceinline__ const float* mt_cos() const { return (const float*)xs0; }
+  __device__ __forceinline__ const float* mt_sin() const { return (const float*)xs1; }
+  __device__ __forceinline__ const int32_t* mt_pos() const {
+    return (const int32_t*)((uint64_t)heads0 << 32 | heads);
   }
-  __device__ __forceinline__ const float* mt_cos() const { return (const float*)xs1; }
-  __device__ __forceinline__ const float* mt_sin() const { return (const float*)((uint64_t)heads0 << 32 | heads); }
+  __device__ __forceinline__ uint32_t mt_xs() const { return div_magic; }
 };
 
 __device__ __forceinline__ uint32_t div_heads(const RowHot& h, uint32_t row) {
@@ -142,7 +146,8 @@ __device__ __forceinline__ Loc locate(const RowParams& p, const RowHot& hp, uint
   Loc r;
   if constexpr (MT) {
     // whole tokens of tensor 0: the pass's first row and token are wave-uniform
-    static_assert(ALIGNED && !POS, "several tokens per pass: aligned, table rows read in order");
+    // (with positions, each lane reads its own token's, see load_input)
+    static_assert(ALIGNED, "several tokens per pass: aligned");
     const uint32_t row0 = __builtin_amdgcn_readfirstlane(pass * (uint32_t)G);
     const uint32_t t = __builtin_amdgcn_readfirstlane(row0 >> hp.tok_shift());
     r.second = false;
@@ -150,7 +155,7 @@ __device__ __forceinline__ Loc locate(const RowParams& p, const RowHot& hp, uint
     r.ri0 = row0;
     r.ri = row0 + slot;
     r.row = row0 + slot;
-    r.xoff = (uint64_t)t * hp.xs0;
+    r.xoff = (uint64_t)t * hp.mt_xs();
   } else if constexpr (ALIGNED) {
     // the whole pass lies inside one token and one tensor, and the launch
     // holds whole passes only: everything but the slot is wave-uniform
@@ -181,7 +186,7 @@ __device__ __forceinline__ Loc locate(const RowParams& p, const RowHot& hp, uint
     r.xoff = (uint64_t)t * (r.second ? hp.xs1 : hp.xs0) + (uint64_t)hk * D;
   }
   r.trow = r.tok;
-  if constexpr (POS) {
+  if constexpr (POS && !MT) {
     // positions outside [0, max_pos) read the last table row (never out of range)
     if constexpr (ALIGNED) {
       // a wave-uniform index: read it through the constant address space (the
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // several tokens, the row's place inside its token otherwise)
   const uint32_t pe_a = slot * D + off_a, pe_b = slot * D + off_b;
   uint32_t px0 = slot * D;
-  if constexpr (MT) px0 = (slot >> hp.tok_shift()) * (uint32_t)hp.xs0 + (slot & ((1u << hp.tok_shift()) - 1u)) * D;
+  if constexpr (MT) px0 = (slot >> hp.tok_shift()) * hp.mt_xs() + (slot & ((1u << hp.tok_shift()) - 1u)) * D;
   const uint32_t px_a = px0 + off_a, px_b = px0 + off_b;
   // passes inside one token: lane l carries bytes [TB l, TB l + TB) of the
   // token's cos row and of its sin row (half <= D / 2 floats: 64 lanes of TB
@@ -280,6 +285,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // the pass's table block: one row, or the rows of its tokens in order
   const uint32_t tpp = MT ? (uint32_t)G >> hp.tok_shift() : 1u;  // tokens per pass
   const uint32_t tbytes = 4u * half * tpp;                      // bytes of the block (cos or sin)
+  // passes of whole tokens: bytes a pass's input rows span (below 2^31, checked
+  // by the launcher)
+  const uint32_t mt_span = MT ? 2u * ((tpp - 1u) * hp.mt_xs() + (1u << hp.tok_shift()) * (uint32_t)D) : 0u;
   const bool t_lane = toff < tbytes;
   float* t_wave = t_lds + (STAGED ? wave * TW : 0);
   // (passes of whole tokens: from the preloaded arguments)
@@ -303,10 +311,21 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // passes of whole tokens: a rope lane's 8 cos and 8 sin values, from its
   // row's token (the pass's tokens are consecutive table rows); plain lanes
   // read outside the block (zero, no memory access)
+  // (with positions: the row its token's position names, clamped into the
+  // table, whose bytes stay below 2^31, checked by the launcher)
   auto load_direct_table = [&](Data& d) {
-    const rsrc_t rc = make_rsrc(cos_tab + (size_t)d.loc.trow * half, tbytes);
-    const rsrc_t rs = make_rsrc(sin_tab + (size_t)d.loc.trow * half, tbytes);
-    const uint32_t o = rope_lane ? 4u * ((slot >> hp.tok_shift()) * half + cs_off) : 0x80000000u;
+    rsrc_t rc, rs;
+    uint32_t o;
+    if constexpr (POS) {
+      const uint32_t trow = min(d.pos, p.max_pos - 1u);
+      rc = make_rsrc(cos_tab, 4u * p.max_pos * half);
+      rs = make_rsrc(sin_tab, 4u * p.max_pos * half);
+      o = rope_lane ? 4u * (trow * half + cs_off) : 0x80000000u;
+    } else {
+      rc = make_rsrc(cos_tab + (size_t)d.loc.trow * half, tbytes);
+      rs = make_rsrc(sin_tab + (size_t)d.loc.trow * half, tbytes);
+      o = rope_lane ? 4u * ((slot >> hp.tok_shift()) * half + cs_off) : 0x80000000u;
+    }
     d.tab.c0 = buf_load16f(rc, o);
     d.tab.c1 = buf_load16f(rc, o + 16u);
     d.tab.s0 = buf_load16f(rs, o);
@@ -315,9 +334,15 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // a pass's input (and, through load_data, its table chunks)
   auto load_input = [&](Data& d, uint32_t pass) {
     d.loc = locate<G, D, ALIGNED, POS, MT>(p, hp, pass, slot);
+    if constexpr (MT && POS) {
+      // this lane's token's position, before the input: the wait for it (ahead
+      // of the table loads) then leaves the input in flight
+      const rsrc_t rp = make_rsrc(hp.mt_pos(), 4u * ((hp.passes * (uint32_t)G) >> hp.tok_shift()));
+      d.pos = buf_load4(rp, 4u * (d.loc.tok + (slot >> hp.tok_shift())));
+    }
     if constexpr (ALIGNED) {
       // the pass's G rows: one wave-uniform descriptor, lane byte offsets
-      const rsrc_t rx = make_rsrc((d.loc.second && !MT ? hp.x1() : hp.x0) + d.loc.xoff, MT ? hp.xspan() : 2u * G * D);
+      const rsrc_t rx = make_rsrc((d.loc.second && !MT ? hp.x1() : hp.x0) + d.loc.xoff, MT ? mt_span : 2u * G * D);
       d.xa = buf_load16_nt(rx, 2u * px_a);
       d.xb = buf_load16_nt(rx, 2u * px_b);
     } else {
@@ -334,7 +359,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     // positions index the row number is itself a load: the table chunks then
     // go out from the middle of the previous pass, see compute.)
     if constexpr (STAGED && !POS) load_staged_table(d);
-    if constexpr (DIRECT) load_direct_table(d);
+    if constexpr (DIRECT && !POS) load_direct_table(d);
   };
   // per-lane rows: every lane loads its own table values (plain lanes read the
   // row start and ignore it); aligned rope passes load theirs with the input
@@ -355,7 +380,10 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   // t: this pass's table values; aligned rope passes stage them in LDS and
   // then load the next pass's table (at `next`) into t.
   // nd: the next pass's data (positions mode: its table chunks are loaded here)
-  auto compute = [&](const Data& s, Table& t, Data& nd, auto opts) {
+  // nxt: whether a next pass follows (a std::integral_constant<bool>); with
+  // positions its table loads go out from the middle of this pass
+  auto compute = [&](const Data& s, Table& t, Data& nd, auto opts, auto nxt) {
+    constexpr bool NEXT = decltype(nxt)::value;
     constexpr bool GEN = decltype(opts)::gen;
     constexpr bool FULL = decltype(opts)::full;  // the rope tail is the whole row: every lane rotates
     constexpr bool XCH = decltype(opts)::xch;
@@ -394,7 +422,8 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     // positions mode: the next pass's table chunks, now that its row number
     // (a scalar load issued with its input) has arrived; still before this
     // pass's stores
-    if constexpr (STAGED && POS) load_staged_table(nd);
+    if constexpr (STAGED && POS && NEXT) load_staged_table(nd);
+    if constexpr (DIRECT && POS && NEXT) load_direct_table(nd);
 
     if constexpr (STAGED) {
       // this pass's cos and sin rows into the wave's LDS slot; a wave's LDS
@@ -561,14 +590,19 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
       wc[i] = *(const uint4*)src;
     }
   }
+  // (the table loads may need kernel-argument fields, such as the table size
+  // with positions: kept after the weights, whose loads need none on passes of
+  // whole tokens)
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (STAGED) {
     // (with positions only the first pass's: each later one goes out from the
     // middle of the pass before it, see compute)
 #pragma unroll
     for (int k = 0; k < (POS ? 1 : NS - 1); ++k) load_staged_table(d[k]);
   } else if constexpr (DIRECT) {
+    // (with positions only the first pass's, as above)
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k) load_direct_table(d[k]);
+    for (int k = 0; k < (POS ? 1 : NS - 1); ++k) load_direct_table(d[k]);
   } else {
     load_table(tb[0], d[0].loc);
   }
@@ -602,33 +636,40 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
   };
 
   auto run = [&](auto opts) {
+    using yes = std::integral_constant<bool, true>;
     uint32_t base = 0;
     for (; base + NS <= n; base += NS) {
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         load_data(d[(k + NS - 1) % NS], pass_of(base + k + NS - 1));
-        if constexpr (STAGED) {
-          compute(d[k], tb[0], d[(k + 1) % NS], opts);
+        if constexpr (STAGED || DIRECT) {
+          compute(d[k], tb[0], d[(k + 1) % NS], opts, yes{});
         } else {
           load_table(tb[(k + 1) % 2], d[(k + 1) % NS].loc);
-          compute(d[k], tb[k % 2], d[k], opts);
+          compute(d[k], tb[k % 2], d[k], opts, yes{});
         }
         progress(base + k + 1);
       }
     }
-    // the last n % NS passes: their input (slots 0 .. NS - 2) and first table are loaded
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k) {
-      if (base + k < n) {
-        const int kn = k + 1 < NS - 1 ? k + 1 : k;  // (the last one reloads its own table)
-        if constexpr (STAGED) {
-          compute(d[k], tb[0], d[kn], opts);
-        } else {
-          if (k + 1 < NS - 1) load_table(tb[(k + 1) % 2], d[k + 1].loc);
-          compute(d[k], tb[k % 2], d[k], opts);
+    // the last n % NS passes: their input (slots 0 .. NS - 2) and first table
+    // are loaded; the final one has no next pass (with positions it loads no
+    // further table rows)
+    auto tail = [&](auto self, auto kc) -> void {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k < NS - 1) {
+        constexpr bool has_next = k + 1 < NS - 1;
+        if (base + k < n) {
+          if constexpr (STAGED || DIRECT) {
+            compute(d[k], tb[0], d[has_next ? k + 1 : k], opts, std::integral_constant<bool, has_next>{});
+          } else {
+            if constexpr (has_next) load_table(tb[(k + 1) % 2], d[k + 1].loc);
+            compute(d[k], tb[k % 2], d[k], opts, std::integral_constant<bool, has_next>{});
+          }
         }
+        self(self, std::integral_constant<int, k + 1>{});
       }
-    }
+    };
+    tail(tail, std::integral_constant<int, 0>{});
   };
   // (XCH only where codes are stored from a wave-uniform base, to 16-byte aligned outputs)
   constexpr bool XQ = QUANT && ALIGNED;

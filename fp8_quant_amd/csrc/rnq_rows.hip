@@ -49,18 +49,18 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   if (p.xs1 == 0) p.xs1 = (uint64_t)(p.heads - p.heads0) * (uint64_t)head_dim;
   const bool pos = p.rope > 0 && p.positions != nullptr;
   // passes of whole tokens of one tensor (G a multiple of the heads per token,
-  // whole passes only, table rows read in order): the tokens of a pass sit at
-  // lane-constant offsets and their table rows form one block of at most 1 KB
-  // per table (16 bytes per lane)
-  if (align == ROWS_PER_LANE && !pos && p.heads0 == p.heads && G % p.heads == 0 && p.total_rows % G == 0) {
+  // whole passes only): the tokens of a pass sit at lane-constant offsets, and
+  // each rope lane reads its own row's table values (with positions: from the
+  // row its token's position names, at 32-bit offsets into the table)
+  if (align == ROWS_PER_LANE && p.heads0 == p.heads && G % p.heads == 0 && p.total_rows % G == 0) {
     uint32_t sh = 0;
     while ((1u << sh) < p.heads) ++sh;
     const uint64_t tpp = G >> sh;
     const uint64_t span = 2 * ((tpp - 1) * p.xs0 + (uint64_t)p.heads * (uint64_t)head_dim);
-    if (span < ((uint64_t)1 << 31) && tpp * (p.rope / 2) * 4 <= 1024) {
+    const bool table_ok = !pos || (uint64_t)p.max_pos * (p.rope / 2) * 4 < ((uint64_t)1 << 31);
+    if (span < ((uint64_t)1 << 31) && p.xs0 < ((uint64_t)1 << 30) && table_ok) {
       align = ROWS_WHOLE_TOKENS;
       p.tok_shift = sh;
-      p.xspan = (uint32_t)span;
     }
   }
   const int mode = (quant ? ROW_QUANT : 0) | (p.rope > 0 ? ROW_ROPE : 0) | (p.y0 != nullptr ? ROW_Y : 0) |

@@ -8,22 +8,21 @@ namespace rnq {
 
 // (the fields a wave needs before its first input load go first, as scalar
 // arguments the hardware preloads; on passes of whole tokens the slots of the
-// second tensor and of the head division carry the weight, cos and sin
-// pointers, the input span and the token shift, as RowHot lays out)
-#define RNQ_ROWS_HOT(p, mt)                                                                                     \
-  (p).x0,                                                                                                       \
-      (mt) ? ((uint64_t)(p).xspan << 32 | (uint32_t)(uintptr_t)(p).w0) : (uint64_t)(uintptr_t)(p).x1, (p).xs0, \
-      (mt) ? (uint64_t)(uintptr_t)(p).cos : (p).xs1, (p).waves, (p).passes,                                     \
-      (mt) ? (uint32_t)(uintptr_t)(p).sin : (p).heads, (mt) ? (uint32_t)((uintptr_t)(p).sin >> 32) : (p).heads0, \
-      (mt) ? (uint32_t)((uintptr_t)(p).w0 >> 32) : (p).div_magic, ((mt) ? (p).tok_shift : (p).div_shift) | (p).rope << 8, (p)
+// second tensor, the token strides and the head division carry the weight,
+// cos, sin and positions pointers, the token stride and the token shift, as
+// RowHot lays out)
+#define RNQ_ROWS_HOT(p, mt)                                                                                       \
+  (p).x0, (mt) ? (uint64_t)(uintptr_t)(p).w0 : (uint64_t)(uintptr_t)(p).x1,                                       \
+      (mt) ? (uint64_t)(uintptr_t)(p).cos : (p).xs0, (mt) ? (uint64_t)(uintptr_t)(p).sin : (p).xs1, (p).waves,     \
+      (p).passes, (mt) ? (uint32_t)(uintptr_t)(p).positions : (p).heads,                                           \
+      (mt) ? (uint32_t)((uintptr_t)(p).positions >> 32) : (p).heads0, (mt) ? (uint32_t)(p).xs0 : (p).div_magic,    \
+      ((mt) ? (p).tok_shift : (p).div_shift) | (p).rope << 8, (p)
 
 template <class DT, int L, int MODE>
 static hipError_t launch_shape(const RowParams& p, int align, dim3 grid, hipStream_t s) {
-  if constexpr ((MODE & ROW_POS) == 0) {
-    if (align == ROWS_WHOLE_TOKENS) {
-      hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true, true>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, true));
-      return hipGetLastError();
-    }
+  if (align == ROWS_WHOLE_TOKENS) {
+    hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true, true>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, true));
+    return hipGetLastError();
   }
   if (align == ROWS_ONE_TOKEN)
     hipLaunchKernelGGL((rows_kernel<DT, L, MODE, true>), grid, dim3(RT), 0, s, RNQ_ROWS_HOT(p, false));

@@ -111,6 +111,32 @@ def test_qk_positions_out_of_range_read_the_last_row():
     compare_qk("clamped positions", {"q": q, "k": k}, got, ref)
 
 
+@pytest.mark.parametrize("T,H,D,R,extra", [
+    (24, 4, 128, 128, 8),   # 2 tokens per pass of 8 rows, padded token stride
+    (40, 1, 128, 64, 0),    # one row per token: 8 tokens per pass
+    (36, 2, 256, 128, 16),  # 2 tokens per pass of 4 rows
+    (20, 1, 512, 256, 0),   # 2 tokens per pass of 2 rows
+    (32, 8, 64, 32, 8),     # 2 tokens per pass of 16 rows
+])
+def test_qk_one_tensor_whole_tokens_per_pass_with_positions(T, H, D, R, extra):
+    """One tensor whose passes hold whole tokens (its heads divide the rows per
+    pass): each rope lane gathers its own token's table row; positions below zero
+    or past the table's end read its last row."""
+    q, _, qkv, wq, _ = _fused(T, H, 0, D, seed=T * 11 + H + D, extra=extra)
+    table_rows = T // 2 + 3
+    cos, sin = workloads.rope_table(np.arange(table_rows) * 7 % 8191, R, 10000.0)
+    cos, sin = torch.from_numpy(cos), torch.from_numpy(sin)
+    g = torch.Generator("cpu").manual_seed(T + D)
+    pos = torch.randint(-3, table_rows + 4, (T,), generator=g, dtype=torch.int32)
+    print(f"[strided] one tensor, whole tokens per pass: T{T} H{H} D{D} R{R} extra {extra}", flush=True)
+    qv, _ = _views(gpu(qkv), T, H, 0, D)
+    got = _run_ex(qv, None, gpu(wq), None, gpu(cos), gpu(sin), gpu(pos), with_y=True)
+    p = pos.numpy().astype(np.int64)
+    rows = np.where((p < 0) | (p >= table_rows), table_rows - 1, p)
+    ref = _oracle(q, None, wq, None, cos, sin, rows)
+    compare_qk(f"one tensor T{T} H{H} D{D}", {"q": q, "k": None}, got, ref)
+
+
 def test_qk_4k_fused_full_size_matches_contiguous_entry():
     """The fused-QKV workload at full size: bit-identical to the contiguous entry on
     gathered tables (the same arithmetic), and to the oracle on sampled tokens."""
@@ -192,6 +218,36 @@ def test_rmsnorm_rope_ex_views(M, N, R, rpt, pad, with_pos):
     ref = oracle.rmsnorm_rope(workloads.bits(x), workloads.bits(w), cos[rows], sin[rows], 1e-6, "bf16", rpt)
     loose = unproven_rows(workloads.bits(x), "bf16")
     assert_rows_match(f"rmsnorm_rope_ex M{M} N{N}", workloads.bits(y), None, None, ref, None, None, loose)
+
+
+@pytest.mark.parametrize("M,N,R,rpt,pad", [
+    (256, 128, 64, 1, 0),   # 8 tokens per pass
+    (128, 64, 32, 4, 8),    # 4 tokens per pass of 16 rows, padded token stride
+    (96, 256, 128, 2, 16),  # 2 tokens per pass of 4 rows
+])
+def test_rmsnorm_rope_whole_tokens_per_pass_positions_out_of_range(M, N, R, rpt, pad):
+    """Path R with positions on passes of whole tokens: every lane gathers its
+    token's table row; out-of-range positions read the table's last row."""
+    T = M // rpt
+    g = torch.Generator("cpu").manual_seed(M * 3 + N + R)
+    x = torch.randn(M, N, generator=g).to(torch.float16)
+    w = (1 + 0.1 * torch.randn(N, generator=g)).to(torch.float16)
+    buf = torch.randn(T, rpt * N + pad, generator=g).to(torch.float16)
+    buf[:, : rpt * N] = x.view(T, rpt * N)
+    table_rows = T // 3 + 2
+    cos, sin = workloads.rope_table(np.arange(table_rows) * 5, R, 10000.0)
+    pos = torch.randint(-4, table_rows + 5, (T,), generator=g, dtype=torch.int32)
+    print(f"[strided] rmsnorm_rope whole tokens per pass M{M} N{N} R{R} rpt{rpt} pad{pad}", flush=True)
+    bg = gpu(buf)
+    xv = bg[:, : rpt * N].view(T, rpt, N) if rpt > 1 else bg[:, :N]
+    y = rnq.rmsnorm_rope(xv, gpu(w), gpu(torch.from_numpy(cos)), gpu(torch.from_numpy(sin)), rows_per_token=rpt,
+                         positions=gpu(pos))
+    torch.cuda.synchronize()
+    p = pos.numpy().astype(np.int64)
+    rows = np.where((p < 0) | (p >= table_rows), table_rows - 1, p)
+    ref = oracle.rmsnorm_rope(workloads.bits(x), workloads.bits(w), cos[rows], sin[rows], 1e-6, "fp16", rpt)
+    loose = unproven_rows(workloads.bits(x), "fp16")
+    assert_rows_match(f"rmsnorm_rope whole tokens M{M} N{N}", workloads.bits(y), None, None, ref, None, None, loose)
 
 
 def test_strided_invalid_arguments_raise():
