@@ -32,8 +32,16 @@ namespace rnq {
 constexpr int NB = 1024;      // threads per workgroup
 constexpr int NBW = NB / 64;  // waves
 
+// (the fields its first loads need come as leading scalar arguments, 14 dwords
+// that gfx950 preloads into scalar registers: x, grad_y, w, cos, sin, M, rows
+// per block, the row -> token magic, and its shift with the rope width; a
+// struct argument is not preloaded, and every wave would first wait for a load
+// of it)
 template <class DT, int D, bool ROPE, bool SAVED>
-__global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
+__global__ __launch_bounds__(NB) void narrow_bwd_kernel(const uint16_t* x_in, const uint16_t* gy_in,
+                                                        const uint16_t* w_in, const float* cos_in,
+                                                        const float* sin_in, uint32_t M, uint32_t rows_per_block,
+                                                        uint32_t div_magic, uint32_t shift_rope, WideBwdParams p) {
   constexpr int L = D / 8;      // lanes per row
   constexpr int G = 64 / L;     // rows per wave
   constexpr int RPI = NBW * G;  // rows per step of the workgroup
@@ -45,37 +53,43 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
   const uint32_t lane = tid & 63;
   const uint32_t ch = lane % L;                    // chunk within the row
   const uint32_t lrow = (tid >> 6) * G + lane / L;  // row within a step
-  const uint32_t r0 = blockIdx.x * p.rows_per_block;
+  const uint32_t div_shift = shift_rope & 0xffu, rope = shift_rope >> 8;
+  const uint32_t r0 = blockIdx.x * rows_per_block;
   // (bwd_blocks' partition gives every block rows; a block without rows would
   // read nothing and write a zero partial row. No early exit: a branch here
   // would come before the kernel-argument loads, and the compiler issues none
   // past a branch.)
-  const uint32_t nrows = r0 < p.M ? min(p.rows_per_block, p.M - r0) : 0u;
+  const uint32_t nrows = r0 < M ? min(rows_per_block, M - r0) : 0u;
   const uint32_t steps = (nrows + RPI - 1) / RPI;
   const uint32_t span = nrows * row_bytes;  // < 2^31 (checked by the caller)
-  const rsrc_t rx = make_rsrc(p.x + (size_t)r0 * D, span);
-  const rsrc_t rg = make_rsrc(p.gy + (size_t)r0 * D, span);
-  const rsrc_t rdx = make_rsrc(p.gx + (size_t)r0 * D, span);
-  const rsrc_t rrs = make_rsrc(p.rstd + r0, SAVED ? 4u * nrows : 0u);
-  const rsrc_t rc = make_rsrc(p.cos, ROPE ? p.table_bytes : 0u);
-  const rsrc_t rs = make_rsrc(p.sin, ROPE ? p.table_bytes : 0u);
+  const rsrc_t rx = make_rsrc(x_in + (size_t)r0 * D, span);
+  const rsrc_t rg = make_rsrc(gy_in + (size_t)r0 * D, span);
+  // one table row per token: tokens = (M - 1) / rows_per_token + 1
+  const uint32_t table_bytes =
+      ROPE ? ((uint32_t)(((uint64_t)(M - 1) * div_magic) >> div_shift) + 1u) * (rope / 2) * 4u : 0u;
+  const rsrc_t rc = make_rsrc(cos_in, table_bytes);
+  const rsrc_t rs = make_rsrc(sin_in, table_bytes);
 
-  float w[8];
-  unpack8<DT>(buf_load16(make_rsrc(p.w, row_bytes), 16u * ch), w);
+  // (kept packed and unpacked in each step: a wait for it ahead of the loop
+  // would hold back the second step's loads)
+  const uint4 w_raw = buf_load16(make_rsrc(w_in, row_bytes), 16u * ch);
 
   // RoPE geometry of this lane's chunk (row-independent)
   bool tail = false, lo_half = false;
   uint32_t pj = 0;
   int src = (int)lane;
   if constexpr (ROPE) {
-    const uint32_t t0 = (D - p.rope) / 8, hc = p.rope / 16;
+    const uint32_t t0 = (D - rope) / 8, hc = rope / 16;
     tail = ch >= t0;
     const uint32_t j = ch - t0;
     lo_half = tail && j < hc;
     pj = lo_half ? j : j - hc;
     src = tail ? (int)lane + (lo_half ? (int)hc : -(int)hc) : (int)lane;
   }
-  const uint32_t half = p.rope / 2;
+  const uint32_t half = rope / 2;
+  // (grad_x and rstd are not preloaded: their descriptors come from the
+  // argument struct, loaded while the first step's loads are in flight)
+  rsrc_t rdx, rrs;
 
   struct In {
     uint4 x, g;
@@ -87,16 +101,16 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
     const uint32_t off = lr * row_bytes + 16u * ch;
     in.x = buf_load16_nt(rx, off);
     in.g = buf_load16_nt(rg, off);
-    if constexpr (SAVED) in.rs = buf_load4f(rrs, 4u * lr);
     if constexpr (ROPE) {
       const uint32_t row = r0 + lr;
-      const uint32_t t = (uint32_t)(((uint64_t)row * p.div_magic) >> p.div_shift);
+      const uint32_t t = (uint32_t)(((uint64_t)row * div_magic) >> div_shift);
       const uint32_t toff = tail ? 4u * (t * half + 8u * pj) : kOutOfRange;
       in.c0 = buf_load16f(rc, toff);
       in.c1 = buf_load16f(rc, toff + 16u);
       in.s0 = buf_load16f(rs, toff);
       in.s1 = buf_load16f(rs, toff + 16u);
     }
+    if constexpr (SAVED) in.rs = buf_load4f(rrs, 4u * lr);
   };
 
   float dw[8];
@@ -106,9 +120,14 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
   auto compute = [&](uint32_t step, const In& in) {
     const uint32_t lr = step * RPI + lrow;
     const bool real = lr < nrows;
-    float xf[8], gn[8];
+    float xf[8], gn[8], w[8];
     unpack8<DT>(in.x, xf);
     unpack8<DT>(in.g, gn);
+    // (an empty asm keeps the weights' unpacking in the step: hoisted out of
+    // the loop it would wait for them before the next step's loads go out)
+    uint4 wr = w_raw;
+    asm volatile("" : "+v"(wr.x), "+v"(wr.y), "+v"(wr.z), "+v"(wr.w));
+    unpack8<DT>(wr, w);
     float rstd;
     if constexpr (SAVED) {
       rstd = in.rs;
@@ -154,7 +173,12 @@ __global__ __launch_bounds__(NB) void narrow_bwd_kernel(WideBwdParams p) {
   };
 
   In a, b;
+  // (the first step's input and table loads need only preloaded arguments; its
+  // saved rstd, if any, waits for the argument struct)
+  rrs = make_rsrc(p.rstd + r0, SAVED ? 4u * nrows : 0u);
   load(0, a);
+  __builtin_amdgcn_sched_barrier(0);
+  rdx = make_rsrc(p.gx + (size_t)r0 * D, span);
   uint32_t s = 0;
   for (; s + 2 <= steps; s += 2) {
     load(s + 1, b);
@@ -193,9 +217,11 @@ bool narrow_bwd_width(int64_t N) { return N == 64 || N == 128 || N == 256 || N =
 template <class DT, int D, bool ROPE>
 static void launch_saved(const WideBwdParams& p, hipStream_t s) {
   if (p.rstd != nullptr)
-    hipLaunchKernelGGL((narrow_bwd_kernel<DT, D, ROPE, true>), dim3(p.blocks), dim3(NB), 0, s, p);
+    hipLaunchKernelGGL((narrow_bwd_kernel<DT, D, ROPE, true>), dim3(p.blocks), dim3(NB), 0, s, p.x, p.gy, p.w, p.cos,
+                       p.sin, p.M, p.rows_per_block, p.div_magic, p.div_shift | p.rope << 8, p);
   else
-    hipLaunchKernelGGL((narrow_bwd_kernel<DT, D, ROPE, false>), dim3(p.blocks), dim3(NB), 0, s, p);
+    hipLaunchKernelGGL((narrow_bwd_kernel<DT, D, ROPE, false>), dim3(p.blocks), dim3(NB), 0, s, p.x, p.gy, p.w, p.cos,
+                       p.sin, p.M, p.rows_per_block, p.div_magic, p.div_shift | p.rope << 8, p);
 }
 
 template <class DT, int D>
