@@ -67,7 +67,7 @@ def measured_traffic():
 # ------------------------------------------------------------------ GPU timing
 
 
-def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS, lead_ms=LEAD_MS):
+def _timed(torch, launches, steps, warmup, warm_ms=None, lead_ms=LEAD_MS):
     """Warm up (``warmup`` launches, and at least ``warm_ms`` of back-to-back
     work, so that every path is timed past the power-management transient at
     the onset of load, whatever its launch length), then time ``steps``
@@ -82,6 +82,8 @@ def _timed(torch, launches, steps, warmup, warm_ms=WARM_MS, lead_ms=LEAD_MS):
     on a busy GPU with the host already ahead of it: the host-side latency of
     submitting the first launch then falls outside the window, which matters
     when only a few steps are timed."""
+    if warm_ms is None:
+        warm_ms = WARM_MS
     n = len(launches)
     t0 = time.perf_counter()
     i = 0
@@ -528,9 +530,13 @@ def main() -> int:
     ap.add_argument("--only", default="",
                     help="comma-separated paths to time alone, each with its same-run floor (one of: "
                          + ", ".join(ONLY_PATHS) + "); prints their summaries")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="least warm-up of back-to-back launches per timed path, in ms (default %(default)s: past the "
+                         "power-management transient; counter passes, which do not time, can take 0)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 256 MiB device copy three times (counter calibration) and exit")
     args = ap.parse_args()
+    globals()["WARM_MS"] = args.warm_ms  # (read by _timed at each call)
 
     if args.calibrate_copy:
         import torch
