@@ -250,6 +250,41 @@ def test_rmsnorm_rope_whole_tokens_per_pass_positions_out_of_range(M, N, R, rpt,
     assert_rows_match(f"rmsnorm_rope whole tokens M{M} N{N}", workloads.bits(y), None, None, ref, None, None, loose)
 
 
+@pytest.mark.parametrize("past", [False, True])
+def test_rmsnorm_rope_positions_table_near_2gib(past):
+    """Whole-token passes gather table rows at 32-bit byte offsets: a table just below
+    2 GiB per half takes that path with rows near its end, one just past it the
+    per-lane layout (64-bit addressing). Only the rows the positions name are written."""
+    M, N, R, rpt = 64, 128, 64, 1
+    half = R // 2
+    limit = (1 << 31) // (4 * half)  # table rows at which one table reaches 2 GiB
+    table_rows = limit + 8 if past else limit - 1
+    g = torch.Generator("cpu").manual_seed(991 + past)
+    x = torch.randn(M, N, generator=g).to(torch.float16)
+    w = (1 + 0.1 * torch.randn(N, generator=g)).to(torch.float16)
+    last = table_rows - 1
+    pos = torch.tensor([last, last - 1, 0, 5, last - 77, table_rows, -1, last - 3] * (M // 8), dtype=torch.int32)
+    rows = np.where((pos.numpy() < 0) | (pos.numpy() >= table_rows), last, pos.numpy()).astype(np.int64)
+    used = np.unique(rows)
+    cu, su = workloads.rope_table(used % 8191 + 1, R, 10000.0)
+    print(f"[strided] table of {table_rows} rows ({'past' if past else 'below'} 2 GiB per half)", flush=True)
+    cos_g = torch.empty((table_rows, half), dtype=torch.float32, device="cuda")
+    sin_g = torch.empty((table_rows, half), dtype=torch.float32, device="cuda")
+    idx = torch.from_numpy(used).cuda()
+    cos_g[idx] = torch.from_numpy(cu).cuda()
+    sin_g[idx] = torch.from_numpy(su).cuda()
+    y = rnq.rmsnorm_rope(gpu(x), gpu(w), cos_g, sin_g, rows_per_token=rpt, positions=gpu(pos))
+    torch.cuda.synchronize()
+    where = {r: i for i, r in enumerate(used)}
+    sel = np.array([where[r] for r in rows])
+    ref = oracle.rmsnorm_rope(workloads.bits(x), workloads.bits(w), cu[sel], su[sel], 1e-6, "fp16", rpt)
+    del cos_g, sin_g
+    torch.cuda.empty_cache()
+    loose = unproven_rows(workloads.bits(x), "fp16")
+    assert_rows_match(f"rmsnorm_rope table near 2 GiB past={past}", workloads.bits(y), None, None, ref, None, None,
+                      loose)
+
+
 def test_strided_invalid_arguments_raise():
     T, Hq, Hk, D = 8, 2, 2, 128
     q, k, qkv, wq, wk = _fused(T, Hq, Hk, D, seed=503)
