@@ -111,18 +111,21 @@ def test_qk_positions_out_of_range_read_the_last_row():
     compare_qk("clamped positions", {"q": q, "k": k}, got, ref)
 
 
-@pytest.mark.parametrize("T,H,D,R,extra", [
-    (24, 4, 128, 128, 8),   # 2 tokens per pass of 8 rows, padded token stride
-    (40, 1, 128, 64, 0),    # one row per token: 8 tokens per pass
-    (36, 2, 256, 128, 16),  # 2 tokens per pass of 4 rows
-    (20, 1, 512, 256, 0),   # 2 tokens per pass of 2 rows
-    (32, 8, 64, 32, 8),     # 2 tokens per pass of 16 rows
+@pytest.mark.parametrize("T,H,D,R,extra,with_y,dtype", [
+    (24, 4, 128, 128, 8, True, torch.bfloat16),   # 2 tokens per pass of 8 rows, padded token stride
+    (40, 1, 128, 64, 0, True, torch.bfloat16),    # one row per token: 8 tokens per pass
+    (36, 2, 256, 128, 16, True, torch.bfloat16),  # 2 tokens per pass of 4 rows
+    (20, 1, 512, 256, 0, True, torch.bfloat16),   # 2 tokens per pass of 2 rows
+    (32, 8, 64, 32, 8, True, torch.bfloat16),     # 2 tokens per pass of 16 rows
+    (24, 4, 128, 128, 0, False, torch.bfloat16),  # codes and scales only
+    (40, 2, 128, 32, 8, False, torch.float16),    # fp16, rope on the last quarter
+    (48, 1, 64, 64, 0, True, torch.float16),      # fp16, one row per token: 16 tokens per pass
 ])
-def test_qk_one_tensor_whole_tokens_per_pass_with_positions(T, H, D, R, extra):
+def test_qk_one_tensor_whole_tokens_per_pass_with_positions(T, H, D, R, extra, with_y, dtype):
     """One tensor whose passes hold whole tokens (its heads divide the rows per
     pass): each rope lane gathers its own token's table row; positions below zero
     or past the table's end read its last row."""
-    q, _, qkv, wq, _ = _fused(T, H, 0, D, seed=T * 11 + H + D, extra=extra)
+    q, _, qkv, wq, _ = _fused(T, H, 0, D, seed=T * 11 + H + D, dtype=dtype, extra=extra)
     table_rows = T // 2 + 3
     cos, sin = workloads.rope_table(np.arange(table_rows) * 7 % 8191, R, 10000.0)
     cos, sin = torch.from_numpy(cos), torch.from_numpy(sin)
@@ -130,11 +133,11 @@ def test_qk_one_tensor_whole_tokens_per_pass_with_positions(T, H, D, R, extra):
     pos = torch.randint(-3, table_rows + 4, (T,), generator=g, dtype=torch.int32)
     print(f"[strided] one tensor, whole tokens per pass: T{T} H{H} D{D} R{R} extra {extra}", flush=True)
     qv, _ = _views(gpu(qkv), T, H, 0, D)
-    got = _run_ex(qv, None, gpu(wq), None, gpu(cos), gpu(sin), gpu(pos), with_y=True)
+    got = _run_ex(qv, None, gpu(wq), None, gpu(cos), gpu(sin), gpu(pos), with_y=with_y)
     p = pos.numpy().astype(np.int64)
     rows = np.where((p < 0) | (p >= table_rows), table_rows - 1, p)
     ref = _oracle(q, None, wq, None, cos, sin, rows)
-    compare_qk(f"one tensor T{T} H{H} D{D}", {"q": q, "k": None}, got, ref)
+    compare_qk(f"one tensor T{T} H{H} D{D}", {"q": q, "k": None}, got, ref, dtype=DT[dtype])
 
 
 def test_qk_4k_fused_full_size_matches_contiguous_entry():
