@@ -23,7 +23,9 @@
 //    again.
 //  * Software pipeline: the input chunks of the next NS - 1 passes (with their
 //    cos/sin chunks on aligned rope passes) and, on per-lane rows, the cos/sin
-//    values of the next pass are in flight while a pass is computed.
+//    values of the next pass are in flight while a pass is computed; with
+//    positions, the next pass's position comes with its input and its table
+//    values go out from the middle of the current pass.
 //    No memory access in the steady state is conditional (clamped indices,
 //    every lane of a row storing the same scale), so the in-order memory
 //    counter can be waited on precisely.
@@ -37,13 +39,15 @@
 //    lane-constant offsets, their table rows are consecutive, and each rope
 //    lane loads its own row's 8 cos and 8 sin values with the pass's input (the
 //    rows of such a pass have tokens of their own: nothing to share through
-//    LDS). Otherwise each lane locates its own row.
+//    LDS). Such launches are short, so the weight, cos, sin and positions
+//    pointers ride in preloaded argument slots (RowHot). Otherwise each lane
+//    locates its own row.
 //  * Inputs may be views: the rows of a token are contiguous in each input
 //    tensor, and consecutive tokens are xs0 / xs1 elements apart (q and k
 //    inside a fused QKV projection output). Outputs are contiguous.
 //  * The cos/sin row of token t is row t, or row positions[t] of a
 //    position-indexed table (clamped into it), gathered as it is read.
-//  * The two weight vectors are staged once per workgroup in LDS (fp32).
+//  * Each wave stages its own copy of the two weight vectors in LDS (fp32).
 //  * Row sums: sum of squares in fp64 (exact for 16-bit inputs) and the
 //    absmax, each reduced over the L lanes with DPP.
 //  * Workgroups are renumbered so that neighbouring row ranges (which share
