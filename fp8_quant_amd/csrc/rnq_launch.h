@@ -161,6 +161,29 @@ inline bool fp8_clamp_needed(float fp8_max) {
   return e4m3_magnitude_host((double)fp8_max * (1.0 + 0x1p-20)) != e4m3_magnitude_host((double)fp8_max);
 }
 
+// How a row-kernel launch's passes of G rows sit in the rows: each lane
+// locates its own row, a pass lies inside one token of one tensor (both head
+// counts multiples of G), or a pass holds whole tokens of one tensor (G a
+// multiple of the heads per token, whole passes only, the pass's input span
+// below 2^31 bytes, and with positions a cos/sin table below 2^31 bytes, since
+// such passes gather table rows at 32-bit offsets). For the last, tok_shift =
+// log2(heads per token). Inputs: the token stride xs0 in elements (as the
+// launcher fills it), the rope width (0: none) and whether positions are given.
+enum RowsAlign : int { ROWS_PER_LANE = 0, ROWS_ONE_TOKEN = 1, ROWS_WHOLE_TOKENS = 2 };
+inline int rows_layout(uint32_t G, uint32_t heads, uint32_t heads0, uint32_t total_rows, uint64_t xs0,
+                       uint32_t head_dim, uint32_t rope, bool pos, uint32_t max_pos, uint32_t* tok_shift) {
+  if (heads % G == 0 && heads0 % G == 0) return ROWS_ONE_TOKEN;
+  if (heads0 != heads || G % heads != 0 || total_rows % G != 0) return ROWS_PER_LANE;
+  uint32_t sh = 0;
+  while ((1u << sh) < heads) ++sh;
+  const uint64_t tpp = G >> sh;
+  const uint64_t span = 2 * ((tpp - 1) * xs0 + (uint64_t)heads * (uint64_t)head_dim);
+  const bool table_ok = !pos || (uint64_t)max_pos * (rope / 2) * 4 < ((uint64_t)1 << 31);
+  if (span >= ((uint64_t)1 << 31) || xs0 >= ((uint64_t)1 << 30) || !table_ok) return ROWS_PER_LANE;
+  *tok_shift = sh;
+  return ROWS_WHOLE_TOKENS;
+}
+
 // Measurement baselines (rnq_baselines.hip): steps 2 and 3 of the unfused
 // norm -> rope -> quant plan, and the chapter 28 designs (rows_per_block rows
 // per workgroup, lookups staged once per workgroup).

@@ -690,9 +690,7 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
     run(Opts<false, false>{});
 }
 
-// How a launch's passes sit in the rows: each lane locates its own row, a
-// pass inside one token of one tensor, or a pass of whole tokens of one tensor.
-enum RowsAlign : int { ROWS_PER_LANE = 0, ROWS_ONE_TOKEN = 1, ROWS_WHOLE_TOKENS = 2 };
+// (how a launch's passes sit in the rows: RowsAlign, rnq_launch.h)
 
 template <int MODE>
 hipError_t launch_rows_mode(const RowParams& p, int head_dim, bool bf16, int align, dim3 grid, hipStream_t s);

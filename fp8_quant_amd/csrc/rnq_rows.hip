@@ -21,9 +21,6 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   p.passes = (uint32_t)((p.total_rows + G - 1) / G);
   // t = row / heads by multiply-shift (exact for every row < 2^31)
   div_magic_for(p.heads, p.div_magic, p.div_shift);
-  // passes stay inside one token and one tensor when both head counts are
-  // multiples of G (then total_rows is a multiple of G too: whole passes only)
-  int align = p.heads % G == 0 && p.heads0 % G == 0 ? ROWS_ONE_TOKEN : ROWS_PER_LANE;
   // the same number of passes for every wave: as few waves as keep the
   // SIMDs busy, at most RNQ_ROWS_MAX_PER_WAVE passes each. Waves that do not
   // fit at once start as others retire, in launch order, so the active
@@ -48,21 +45,12 @@ hipError_t launch_rows(RowParams p, int head_dim, bool bf16, bool quant, hipStre
   if (p.xs0 == 0) p.xs0 = (uint64_t)p.heads0 * (uint64_t)head_dim;
   if (p.xs1 == 0) p.xs1 = (uint64_t)(p.heads - p.heads0) * (uint64_t)head_dim;
   const bool pos = p.rope > 0 && p.positions != nullptr;
-  // passes of whole tokens of one tensor (G a multiple of the heads per token,
-  // whole passes only): the tokens of a pass sit at lane-constant offsets, and
-  // each rope lane reads its own row's table values (with positions: from the
-  // row its token's position names, at 32-bit offsets into the table)
-  if (align == ROWS_PER_LANE && p.heads0 == p.heads && G % p.heads == 0 && p.total_rows % G == 0) {
-    uint32_t sh = 0;
-    while ((1u << sh) < p.heads) ++sh;
-    const uint64_t tpp = G >> sh;
-    const uint64_t span = 2 * ((tpp - 1) * p.xs0 + (uint64_t)p.heads * (uint64_t)head_dim);
-    const bool table_ok = !pos || (uint64_t)p.max_pos * (p.rope / 2) * 4 < ((uint64_t)1 << 31);
-    if (span < ((uint64_t)1 << 31) && p.xs0 < ((uint64_t)1 << 30) && table_ok) {
-      align = ROWS_WHOLE_TOKENS;
-      p.tok_shift = sh;
-    }
-  }
+  // passes inside one token and one tensor (both head counts multiples of G,
+  // whole passes then), passes of whole tokens of one tensor (their rows at
+  // lane-constant offsets, each rope lane reading its own row's table values,
+  // with positions at 32-bit offsets into the table), or rows located per lane
+  const int align = rows_layout(G, p.heads, p.heads0, p.total_rows, p.xs0, (uint32_t)head_dim, p.rope, pos,
+                                p.max_pos, &p.tok_shift);
   const int mode = (quant ? ROW_QUANT : 0) | (p.rope > 0 ? ROW_ROPE : 0) | (p.y0 != nullptr ? ROW_Y : 0) |
                    (p.rstd != nullptr ? ROW_RSTD : 0) | (pos ? ROW_POS : 0);
   switch (mode) {

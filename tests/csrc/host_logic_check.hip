@@ -4,7 +4,11 @@
 //           every multiple of d near the top and the rows around them;
 //   clamp - for each fp8_max given on the command line (as a decimal), whether
 //           the launchers clamp quotients before encoding (fp8_clamp_needed),
-//           printed as "<fp8_max> <0|1>" for the caller to compare.
+//           printed as "<fp8_max> <0|1>" for the caller to compare;
+//   layout - for each line "G heads heads0 total_rows xs0 head_dim rope pos
+//           max_pos" on stdin, the row kernel's pass layout (rows_layout),
+//           printed as "<layout> <tok_shift>" (tok_shift -1 unless whole
+//           tokens) for the caller to compare.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -46,6 +50,17 @@ int main(int argc, char** argv) {
     }
     return 0;
   }
-  fprintf(stderr, "usage: host_logic_check div | clamp <fp8_max>...\n");
+  if (argc >= 2 && strcmp(argv[1], "layout") == 0) {
+    unsigned G, heads, heads0, rows, head_dim, rope, pos, max_pos;
+    unsigned long long xs0;
+    while (scanf("%u %u %u %u %llu %u %u %u %u", &G, &heads, &heads0, &rows, &xs0, &head_dim, &rope, &pos,
+                 &max_pos) == 9) {
+      uint32_t sh = 0xffffffffu;
+      const int a = rnq::rows_layout(G, heads, heads0, rows, xs0, head_dim, rope, pos != 0, max_pos, &sh);
+      printf("%d %d\n", a, a == rnq::ROWS_WHOLE_TOKENS ? (int)sh : -1);
+    }
+    return 0;
+  }
+  fprintf(stderr, "usage: host_logic_check div | clamp <fp8_max>... | layout < cases\n");
   return 2;
 }
