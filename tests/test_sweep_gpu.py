@@ -13,7 +13,7 @@ import fp8_quant_amd as rnq
 import oracle
 import workloads
 
-from _parity import compare_qk, gpu, run_qk_gpu, oracle_qk, unproven_rows
+from _parity import assert_rows_match, compare_qk, gpu, run_qk_gpu, oracle_qk, unproven_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -135,3 +135,53 @@ def test_wide_bwd_random_shapes(seed):
     err = np.abs(dx - ref_dx) / (np.abs(ref_dx) + np.sqrt((ref_dx**2).mean(axis=1, keepdims=True)))
     errw = np.abs(gw.cpu().numpy() - ref_dw) / (np.abs(ref_dw) + np.sqrt((ref_dw**2).mean()))
     assert err.max() <= 2e-2 and errw.max() <= 2e-2, (err.max(), errw.max())
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_whole_token_positions_random(seed):
+    """Path R and one-tensor prologues whose passes hold whole tokens (the heads per
+    token divide the rows per pass), cos/sin gathered through positions that run
+    below zero and past the table (clamped to its last row), in padded token-strided
+    views."""
+    rng = np.random.default_rng(5000 + seed)
+    D = int(rng.choice([64, 128, 256, 512]))
+    G = 1024 // D  # rows per pass
+    heads = int(rng.choice([h for h in (1, 2, 4, 8) if h < G]))
+    T = (G // heads) * int(rng.integers(1, 12))
+    R = int(rng.choice([r for r in (16, 32, 64, D) if r <= D]))
+    dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float16
+    pad = int(rng.choice([0, 8, 24]))
+    table_rows = int(rng.integers(1, 3 * T + 1))
+    quant = bool(rng.random() < 0.5)
+    g = torch.Generator("cpu").manual_seed(500 + seed)
+    x = (torch.randn(T, heads, D, generator=g) * float(rng.choice([0.05, 1.0, 20.0]))).to(dtype)
+    w = (1 + 0.2 * torch.randn(D, generator=g)).to(dtype)
+    buf = torch.zeros(T, heads * D + pad, dtype=dtype)
+    buf[:, : heads * D] = x.reshape(T, -1)
+    pos = torch.from_numpy(rng.integers(-3, table_rows + 4, T).astype(np.int32))
+    cos, sin = workloads.rope_table(rng.integers(0, 100000, table_rows), R, float(rng.choice([1e4, 1e6])))
+    p = pos.numpy().astype(np.int64)
+    rows = np.where((p < 0) | (p >= table_rows), table_rows - 1, p)
+    print(f"[sweep] whole tokens seed {seed}: T{T} heads{heads} D{D} R{R} {DT[dtype]} pad{pad} "
+          f"table {table_rows} {'qk' if quant else 'path R'}", flush=True)
+    xv = gpu(buf)[:, : heads * D].view(T, heads, D)
+    cg, sg = gpu(torch.from_numpy(cos)), gpu(torch.from_numpy(sin))
+    if quant:
+        dev = xv.device
+        q8 = torch.full((T, heads, D), 0xAB, dtype=torch.uint8, device=dev)
+        qs = torch.full((T, heads), float("nan"), device=dev)
+        qy = torch.empty((T, heads, D), dtype=dtype, device=dev) if seed % 2 else None
+        rnq.rnq_qk_norm_rope_fp8_ex(xv, None, gpu(w), None, cg, sg, q8, None, qs, None, qy, None, positions=gpu(pos))
+        torch.cuda.synchronize()
+        got = {"q_codes": q8.cpu().numpy(), "q_scale": qs.cpu().numpy(), "k_codes": None, "k_scale": None,
+               "q_y": None if qy is None else workloads.bits(qy), "k_y": None}
+        ref = oracle.qk_norm_rope_fp8(workloads.bits(x), None, workloads.bits(w), None, cos, sin, dtype=DT[dtype],
+                                      tokens=rows)
+        compare_qk(f"whole tokens seed {seed}", {"q": x, "k": None}, got, ref, DT[dtype])
+    else:
+        y = rnq.rmsnorm_rope(xv if heads > 1 else xv[:, 0], gpu(w), cg, sg, rows_per_token=heads, positions=gpu(pos))
+        torch.cuda.synchronize()
+        ref = oracle.rmsnorm_rope(workloads.bits(x.reshape(-1, D)), workloads.bits(w), cos[rows], sin[rows], 1e-6,
+                                  DT[dtype], heads)
+        loose = unproven_rows(workloads.bits(x.reshape(-1, D)), DT[dtype])
+        assert_rows_match(f"whole tokens seed {seed}", workloads.bits(y), None, None, ref, None, None, loose)
