@@ -166,6 +166,18 @@ __device__ __forceinline__ void buf_store8_nt(rsrc_t r, uint32_t off, uint2 v) {
   const u32x2 w = {v.x, v.y};
   __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);
 }
+// Stores with the sc1 cache-policy bit alone (device scope, no streaming
+// hint). Which store policy suits an output was measured kernel by kernel
+// (builds alternated in one process): device-scope stores made the wide RMSNorm
+// forward's y 12.50 -> 11.67 us at 4096 x 4096, while they made the row
+// kernel's FP8 codes (320 -> 338 us at the 65,536-token prologue), path R's y,
+// the grouped kernel's outputs and the narrow backward's grad_x slower than
+// nontemporal or ordinary stores, which those keep.
+constexpr int kDeviceScope = 16;  // cache-policy bit sc1
+__device__ __forceinline__ void buf_store16_dev(rsrc_t r, uint32_t off, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, kDeviceScope);
+}
 __device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
