@@ -39,7 +39,15 @@ KERNEL_SOURCES = ("fp8_quant_amd/csrc/rnq_rows.h", "fp8_quant_amd/csrc/rnq_rows_
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qk_4k.json")
 WARM_MS = 40.0  # the onset-of-load transient lasts ~15 ms
 LEAD_MS = 0.5  # untimed work queued ahead of the start event
-ROTATE_BYTES = 600 * 2**20  # rotate input/output sets until the working set exceeds the 256 MB cache
+# Rotate input/output sets until they hold at least this many bytes: the inputs
+# must come from HBM, not the 256 MB Infinity Cache, and so must the outputs go
+# to it. Outputs are a third or more of a path's bytes, so 2 GiB of sets keeps
+# them well past the cache too: ordinary and device-scope stores allocate there,
+# and with 600 MB of sets (about 220 MB of outputs) their lines could stay
+# resident and never reach HBM inside the timed window (4096 x 4096 backward:
+# 0.47 us faster with ordinary stores at 600 MB, no faster at 4 GB).
+ROTATE_BYTES = 2 * 2**30
+MAX_SETS = 256
 COPY_BYTES = 256 * 2**20  # size of the plain copy used to calibrate the HBM byte counters
 
 
@@ -108,7 +116,7 @@ def _timed(torch, launches, steps, warmup, warm_ms=None, lead_ms=LEAD_MS):
 
 
 def _n_sets(nbytes: int) -> int:
-    return max(1, min(64, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
+    return max(1, min(MAX_SETS, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
 
 
 def input_hashes(workloads, d, names):
@@ -373,9 +381,10 @@ def _with_floor(torch, summary, steps, warmup):
 
 def bench_floor(torch, total_bytes, steps, warmup, with_empty=True):
     """Memory floors for ``total_bytes`` of traffic, measured the same way as the
-    kernels: rnq_baseline_stream reading 2/3 and writing 1/3 of the bytes
+    kernels: rnq_baseline_stream_policy reading 2/3 and writing 1/3 of the bytes
     (rounded to whole 2 KB blocks; the headline moves 44.0 MB in and 21.6 MB
-    out), no arithmetic, rotated like the headline; the runtime's own
+    out), no arithmetic, rotated like the headline, timed with nontemporal and
+    with device-scope stores (the faster one is the floor); the runtime's own
     device-to-device copy (torch ``copy_``, i.e. hipMemcpyAsync) of half the
     bytes (read once, written once: the same total); and the cost of an empty
     launch."""
@@ -386,7 +395,11 @@ def bench_floor(torch, total_bytes, steps, warmup, with_empty=True):
     dev = torch.device("cuda:0")
     sets = [(torch.empty(src_bytes, dtype=torch.uint8, device=dev).fill_(i + 1),
              torch.empty(src_bytes // 2, dtype=torch.uint8, device=dev)) for i in range(n_sets)]
-    ms = _timed(torch, [baselines.prepare_stream(a, b) for a, b in sets], steps, warmup)
+    # the faster of two store policies (nontemporal, device scope): which one
+    # wins depends on the size
+    ms_nt = _timed(torch, [baselines.prepare_stream(a, b, store_policy=0) for a, b in sets], steps, warmup)
+    ms_dev = _timed(torch, [baselines.prepare_stream(a, b, store_policy=1) for a, b in sets], steps, warmup)
+    ms = min(ms_nt, ms_dev)
     del sets
     torch.cuda.empty_cache()
     moved = src_bytes * 3 // 2
@@ -398,12 +411,14 @@ def bench_floor(torch, total_bytes, steps, warmup, with_empty=True):
     del csets
     torch.cuda.empty_cache()
     out = {"stream_us": round(ms * 1e3, 3), "stream_bytes": moved,
+           "stream_nontemporal_us": round(ms_nt * 1e3, 3), "stream_device_scope_us": round(ms_dev * 1e3, 3),
            "stream_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
            "stream_pct_of_peak": round(100.0 * moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
            "d2d_copy_us": round(ms_copy * 1e3, 3), "d2d_copy_bytes_moved": 2 * copy_bytes,
            "d2d_copy_GB/s": round(2 * copy_bytes / (ms_copy * 1e-3) / 1e9, 1),
            "d2d_copy_pct_of_peak": round(100.0 * 2 * copy_bytes / (ms_copy * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-           "kernel": "rnq_baseline_stream (one 2 KB block in, 1 KB out per wave, 16-byte nontemporal accesses); "
+           "kernel": "rnq_baseline_stream_policy (one 2 KB block in, 1 KB out per wave, 16-byte nontemporal loads; "
+                     "the faster of nontemporal and device-scope stores); "
                      "d2d copy: torch copy_ (hipMemcpyAsync device to device)"}
     if with_empty:
         out["empty_launch_us"] = round(_timed(torch, [baselines.prepare_stream(None)], steps, warmup) * 1e3, 3)

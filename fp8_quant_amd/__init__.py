@@ -85,6 +85,7 @@ EXPORTED_SYMBOLS = (
     "rnq_baseline_qk_design",
     "rnq_baseline_stream",
     "rnq_rmsnorm_rope_bwd_noalloc",
+    "rnq_baseline_stream_policy",
 )
 
 RNQ_BF16 = 0
@@ -148,6 +149,8 @@ def load_library():
     lib.rnq_baseline_qk_design.restype = i32
     lib.rnq_baseline_stream.argtypes = [vp, i64, vp, vp]
     lib.rnq_baseline_stream.restype = i32
+    lib.rnq_baseline_stream_policy.argtypes = [vp, i64, vp, i32, vp]
+    lib.rnq_baseline_stream_policy.restype = i32
     lib.rnq_rmsnorm_rope_bwd_noalloc.argtypes = [vp] * 8 + [i64] * 4 + [f32, i32, vp]
     lib.rnq_rmsnorm_rope_bwd_noalloc.restype = i32
     _lib = lib

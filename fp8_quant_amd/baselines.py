@@ -86,10 +86,11 @@ def qk_design(q, k, wq, wk, cos, sin, *, rows_per_block, eps=1e-6, fp8_max=448.0
     return q8.view(torch.float8_e4m3fn), k8.view(torch.float8_e4m3fn), qs, ks
 
 
-def prepare_stream(src, dst=None, *, stream=None):
+def prepare_stream(src, dst=None, *, store_policy=0, stream=None):
     """The memory floor: reads all of ``src`` (its size a multiple of 2048 bytes) and
-    writes half as many bytes to ``dst``; ``src=None`` gives a launch of one empty
-    workgroup (the cost of a launch). Returns a zero-argument launcher."""
+    writes half as many bytes to ``dst``, stored nontemporal (``store_policy`` 0) or
+    with device scope (1); ``src=None`` gives a launch of one empty workgroup (the
+    cost of a launch). Returns a zero-argument launcher."""
     lib = load_library()
     if src is None:
         s = stream if stream is not None else _torch().cuda.current_stream()
@@ -99,5 +100,6 @@ def prepare_stream(src, dst=None, *, stream=None):
         raise ValueError("dst must hold at least half of src's bytes")
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("src and dst must be contiguous")
-    return _launcher(lib.rnq_baseline_stream, (_ptr(src), nbytes, _ptr(dst), _stream(src, stream)), src, dst)
+    return _launcher(lib.rnq_baseline_stream_policy,
+                     (_ptr(src), nbytes, _ptr(dst), int(store_policy), _stream(src, stream)), src, dst)
 

@@ -602,7 +602,10 @@ rnq_status rnq_baseline_qk_design(const void* q, const void* k, const void* wq, 
                     "rnq_baseline_qk_design");
 }
 
-rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, void* stream) {
+static rnq_status baseline_stream(const char* name, const void* src, int64_t src_bytes, void* dst,
+                                  int store_policy, void* stream) {
+  if (store_policy != 0 && store_policy != 1)
+    return fail(RNQ_ERR_ARG, "store_policy must be 0 (nontemporal) or 1 (device scope), got %d", store_policy);
   if (src_bytes < 0 || src_bytes % 2048 != 0)
     return fail(RNQ_ERR_SHAPE, "src_bytes must be a non-negative multiple of 2048 (got %lld)", (long long)src_bytes);
   if (src_bytes / 2048 >= ((int64_t)1 << 31)) return fail(RNQ_ERR_UNSUPPORTED, "src_bytes / 2048 must stay below 2^31");
@@ -613,8 +616,17 @@ rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, vo
     const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (uintptr_t)(src_bytes / 2);
     if (s0 < d1 && d0 < s1) return fail(RNQ_ERR_ARG, "src and dst overlap");
   }
-  return hip_status(launch_stream(src, dst, (uint32_t)(src_bytes / 2048), (hipStream_t)stream),
-                    "rnq_baseline_stream");
+  return hip_status(launch_stream(src, dst, (uint32_t)(src_bytes / 2048), store_policy == 1, (hipStream_t)stream),
+                    name);
+}
+
+rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, void* stream) {
+  return baseline_stream("rnq_baseline_stream", src, src_bytes, dst, 0, stream);
+}
+
+rnq_status rnq_baseline_stream_policy(const void* src, int64_t src_bytes, void* dst, int store_policy,
+                                      void* stream) {
+  return baseline_stream("rnq_baseline_stream_policy", src, src_bytes, dst, store_policy, stream);
 }
 
 }  // extern "C"

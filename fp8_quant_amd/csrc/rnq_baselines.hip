@@ -302,8 +302,9 @@ hipError_t launch_design(const RowParams& rp, uint32_t rows_per_block, int D, bo
 
 // The memory floor of a byte pattern like the prologue's, for measurement: wave
 // w reads the 2 KB block w of src (two 16-byte chunks per lane, 1 KB apart) and
-// writes the 1 KB block w of dst (their XOR), with nontemporal buffer accesses
-// and nothing else.
+// writes the 1 KB block w of dst (their XOR), with nontemporal loads, stores
+// nontemporal or with device scope (DEV), and nothing else.
+template <bool DEV>
 __global__ __launch_bounds__(256) void stream_kernel(const uint8_t* src, uint8_t* dst, uint32_t blocks) {
   const uint32_t w = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63u;
   // waves past the last block read and write nothing (empty descriptors): an
@@ -315,18 +316,25 @@ __global__ __launch_bounds__(256) void stream_kernel(const uint8_t* src, uint8_t
   const rsrc_t rd = make_rsrc(dst + wb * 1024u, live ? 1024u : 0u);
   const uint4 a = buf_load16_nt(rs, 16u * lane);
   const uint4 b = buf_load16_nt(rs, 1024u + 16u * lane);
-  buf_store16_nt(rd, 16u * lane, make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w));
+  const uint4 v = make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w);
+  if constexpr (DEV)
+    buf_store16_dev(rd, 16u * lane, v);
+  else
+    buf_store16_nt(rd, 16u * lane, v);
 }
 
 // One workgroup that does nothing: the cost of a launch.
 __global__ void empty_kernel() {}
 
-hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s) {
+hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, bool device_scope, hipStream_t s) {
   if (blocks == 0) {
     hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+  } else if (device_scope) {
+    hipLaunchKernelGGL(stream_kernel<true>, dim3((blocks + 3) / 4), dim3(256), 0, s, (const uint8_t*)src,
+                       (uint8_t*)dst, blocks);
   } else {
-    hipLaunchKernelGGL(stream_kernel, dim3((blocks + 3) / 4), dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst,
-                       blocks);
+    hipLaunchKernelGGL(stream_kernel<false>, dim3((blocks + 3) / 4), dim3(256), 0, s, (const uint8_t*)src,
+                       (uint8_t*)dst, blocks);
   }
   return hipGetLastError();
 }

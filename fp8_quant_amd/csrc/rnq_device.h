@@ -168,11 +168,13 @@ __device__ __forceinline__ void buf_store8_nt(rsrc_t r, uint32_t off, uint2 v) {
 }
 // Stores with the sc1 cache-policy bit alone (device scope, no streaming
 // hint). Which store policy suits an output was measured kernel by kernel
-// (builds alternated in one process): device-scope stores made the wide RMSNorm
-// forward's y 12.50 -> 11.67 us at 4096 x 4096, while they made the row
+// (builds alternated in one process, with more rotated output buffers than the
+// 256 MB Infinity Cache holds: ordinary and device-scope stores allocate there,
+// and fewer buffers can stay resident): device-scope stores made the wide
+// RMSNorm forward's y 12.95 -> 12.81 us at 4096 x 4096, while they made the row
 // kernel's FP8 codes (320 -> 338 us at the 65,536-token prologue), path R's y,
 // the grouped kernel's outputs and the narrow backward's grad_x slower than
-// nontemporal or ordinary stores, which those keep.
+// nontemporal stores, which those keep.
 constexpr int kDeviceScope = 16;  // cache-policy bit sc1
 __device__ __forceinline__ void buf_store16_dev(rsrc_t r, uint32_t off, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};

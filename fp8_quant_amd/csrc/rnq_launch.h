@@ -192,7 +192,7 @@ hipError_t launch_unfused_rope_quant(const uint16_t* normed, const float* cos, c
                                      uint32_t rows_per_token, float fp8_max, bool bf16, hipStream_t s);
 hipError_t launch_design(const RowParams& p, uint32_t rows_per_block, int D, bool bf16, hipStream_t s);
 // src_bytes / 2048 blocks of the memory-floor kernel (0: one empty workgroup)
-hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, hipStream_t s);
+hipError_t launch_stream(const void* src, void* dst, uint32_t blocks, bool device_scope, hipStream_t s);
 
 // Deterministic row partition used by the backward (rope_dim > 0: the RoPE
 // backward); the workspace size covers every rope_dim.

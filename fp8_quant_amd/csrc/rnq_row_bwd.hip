@@ -234,15 +234,10 @@ __global__ __launch_bounds__(RBT) void row_bwd_kernel(const uint16_t* x_in, cons
       }
       dw_w[(2 * k) * 64 + lane] = make_float4(d[0], d[1], d[2], d[3]);
       dw_w[(2 * k + 1) * 64 + lane] = make_float4(d[4], d[5], d[6], d[7]);
-      // rows past the range are past the descriptor: the store is dropped.
-      // (Ordinary stores without RoPE, nontemporal ones with it: measured with
-      // builds alternated in one process at 4096 x 4096, 24.07 -> 23.60 us
-      // without RoPE, 24.50 -> 25.07 us with it when ordinary.)
-      const uint32_t doff = lr * row_bytes + 16u * lane + 1024u * k;
-      if constexpr (ROPE)
-        buf_store16_nt(rdx, doff, pack8<DT>(o));
-      else
-        buf_store16(rdx, doff, pack8<DT>(o));
+      // rows past the range are past the descriptor: the store is dropped
+      // (nontemporal: ordinary stores measured no faster once the rotated
+      // outputs exceed the Infinity Cache, and slower with RoPE)
+      buf_store16_nt(rdx, lr * row_bytes + 16u * lane + 1024u * k, pack8<DT>(o));
     }
   };
 

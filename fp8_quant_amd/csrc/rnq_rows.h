@@ -488,8 +488,9 @@ __global__ __launch_bounds__(RT) void rows_kernel(const uint16_t* x0, uint64_t x
       const uint4 ya = H16 ? pack8_bits(h) : pack8<DT>(y);
       const uint4 yb = H16 ? pack8_bits(h + 8) : pack8<DT>(y + 8);
       if constexpr (ALIGNED) {
-        // (nontemporal: path R at 16384 x 128 fp16 4.35 -> 3.91 us against
-        // ordinary stores, builds alternated in one process)
+        // (nontemporal: path R at 16384 x 128 fp16 4.38 -> 3.97 us against
+        // ordinary stores, builds alternated in one process, outputs rotated
+        // past the Infinity Cache)
         const rsrc_t ry = make_rsrc(ybase, 2u * G * D);
         buf_store16_nt(ry, 2u * ea, ya);
         buf_store16_nt(ry, 2u * eb, yb);

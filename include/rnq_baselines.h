@@ -58,6 +58,17 @@ rnq_status rnq_baseline_qk_design(const void* q, const void* k, const void* wq, 
  */
 rnq_status rnq_baseline_stream(const void* src, int64_t src_bytes, void* dst, void* stream);
 
+/*
+ * The same floor with dst stored under a chosen cache policy: store_policy 0 is
+ * nontemporal (as rnq_baseline_stream), 1 is device scope (the sc1 bit alone).
+ * Which is faster depends on the size (measured on MI355X: device scope at tens
+ * to hundreds of MB, nontemporal at a few MB and at gigabytes), so a floor is
+ * the faster of the two. Errors as rnq_baseline_stream, and ARG for another
+ * store_policy.
+ */
+rnq_status rnq_baseline_stream_policy(const void* src, int64_t src_bytes, void* dst, int store_policy,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

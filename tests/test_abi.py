@@ -282,6 +282,11 @@ def test_stream_floor_validation():
     assert f(None, 2048, FAKE, None) == 1
     assert f(ctypes.c_void_p(0x10008), 2048, ctypes.c_void_p(0x20000), None) == 3  # src not 16-byte aligned
     assert f(ctypes.c_void_p(0x10000), 4096, ctypes.c_void_p(0x10800), None) == 4  # dst inside src
+    g = lib.rnq_baseline_stream_policy
+    assert g(FAKE, 2048, FAKE, 2, None) == 4  # store policy other than 0 / 1
+    assert g(FAKE, 2048, FAKE, -1, None) == 4
+    assert g(FAKE, 1000, FAKE, 1, None) == 2
+    assert g(None, 2048, FAKE, 0, None) == 1
 
 
 def test_baseline_entry_validation():
